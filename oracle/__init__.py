@@ -1,0 +1,37 @@
+"""CPU oracle for paged decode attention — TEST INFRASTRUCTURE ONLY.
+
+This package is the plain, slow, float64 statement of what one decode step of
+paged attention computes.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import it; the library path
+(``paged_kv_cache_471_amd``) never does, and it shares no code, tables or
+helpers with the HIP kernels.
+
+What it follows (page titles of the source material):
+
+* One query row per request, attending over that request's whole cached history
+  (OpWeave, App. A.2 "Execution-regime assumptions"; SPLASH, §4.1 step "Handoff"
+  and §4.2, where a decode step has one query row per request).
+* Every query head attends over the complete history; the result is defined up
+  to floating-point reduction order (SPLASH, §3 "Computation").
+* Grouped-query heads share a KV head; MLA keeps one head-shared latent per
+  token with no head axis (SPLASH, §1 and §2).
+* The latent is d_c + d_rope = 512 + 64 = 576 values per token (Analytical
+  Provisioning for Attention-FFN Disaggregated LLM Serving, App. B.1).
+* The KV history is stored in pages and each decode step appends to it
+  (OpWeave, §8 "paged KV-cache management"; Analytical Provisioning, §2 and
+  Fig. 1).
+* FP8 E4M3 KV carries scales (SPLASH, App. C.1 and App. B.1).
+
+Readings taken where the pages are silent are listed in the module docstrings
+of ``attention.py`` and ``plan.py``.
+"""
+from .formats import bf16_bits_to_f64, fp8_e4m3fn_to_f64, fp8_e4m3fn_table, decode_storage
+from .attention import (gather_history, paged_decode_attention, mla_decode_attention,
+                        attention_over_range, lse_merge, dense_attention)
+from .plan import partition, Partition
+
+__all__ = [
+    "bf16_bits_to_f64", "fp8_e4m3fn_to_f64", "fp8_e4m3fn_table", "decode_storage",
+    "gather_history", "paged_decode_attention", "mla_decode_attention",
+    "attention_over_range", "lse_merge", "dense_attention", "partition", "Partition",
+]
