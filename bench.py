@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Benchmark: one decode step of paged attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one call of the library's decode attention over one batch (planner,
+split attention and merge kernels).  The headline workload is the
+Llama-3-8B-shaped GQA batch (64 requests, 32 query / 8 KV heads, head_dim 128,
+bf16, page 16, lognormal lengths with median 2048).  Inputs are seeded and
+synthetic and already resident in HBM when timing starts; two copies of the
+KV cache are alternated so that consecutive steps cannot hit in the 256 MB
+last-level cache.
+
+Printed: one JSON line with the metric (algorithmic KV GB/s), tokens/s, the
+dominant kernel's roofline (its own duration from hipExtLaunchKernel events
+recorded over the timed region), HBM traffic from committed rocprofv3 counter
+runs when they match the current kernel source, the float64 CPU oracle's
+throughput on a bounded sample, and the other workloads as secondary figures.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention KV GB/s (% of HBM peak) + tokens/s per step, 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["paged_kv_cache_471_amd/csrc/gqa.hip", "paged_kv_cache_471_amd/csrc/da_common.h",
+                  "paged_kv_cache_471_amd/csrc/da_launch.h"]
+PMC_FILE = os.path.join(ROOT, "profiles", "gqa_llama8b_pmc.md")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles():
+    """HBM bytes per launch of the GQA kernel from the committed counter summary,
+    or None when the summary is missing or was taken on a different kernel source."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    for line in open(PMC_FILE):
+        if line.startswith("pmc: "):
+            d = json.loads(line[5:])
+            if d.get("kernel_hash") != kernel_hash():
+                return None
+            return d.get("traffic_bytes_per_launch")
+    return None
+
+
+def workload_desc(cfg) -> str:
+    import workloads as wl
+    if isinstance(cfg, wl.MLAConfig):
+        return (f"{cfg.name}: batch {cfg.batch}, {cfg.q_heads} heads over a {cfg.latent_dim}-wide bf16 latent "
+                f"(values {cfg.v_dim}), page {cfg.page_size}, lengths {cfg.lengths}")
+    return (f"{cfg.name}: batch {cfg.batch}, {cfg.q_heads}/{cfg.kv_heads} heads, head_dim {cfg.head_dim}, "
+            f"q {wl.DTYPE_NAMES[cfg.q_dtype]}, kv {wl.DTYPE_NAMES[cfg.kv_dtype]}, page {cfg.page_size}, "
+            f"lengths {cfg.lengths}")
+
+
+class GqaRunner:
+    def __init__(self, cfg, sets=2):
+        import torch
+        import workloads as wl
+        from workloads import accounting
+        self.cfg = cfg
+        t0 = time.time()
+        self.case = wl.make_gqa_case(cfg)
+        self.gen_s = time.time() - t0
+        c = self.case
+        dev = "cuda"
+        to = lambda x, dt: _to_dev(x, dt, dev)
+        self.q = to(c.q, cfg.q_dtype)
+        kv0 = to(c.kv, cfg.kv_dtype)
+        self.kvs = [kv0] + [kv0.clone() for _ in range(sets - 1)]
+        self.pt = torch.from_numpy(c.page_table).to(dev)
+        self.sl = torch.from_numpy(c.seq_lens).to(dev)
+        self.ks = None if c.k_scale is None else torch.from_numpy(c.k_scale).to(dev)
+        self.vs = None if c.v_scale is None else torch.from_numpy(c.v_scale).to(dev)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(self.q.shape[:2], dtype=torch.float32, device=dev)
+        self.bytes = accounting.gqa_bytes(c.seq_lens, cfg.page_size, cfg.q_heads, cfg.kv_heads, cfg.head_dim,
+                                          cfg.q_dtype, cfg.kv_dtype)
+        self.flops = accounting.gqa_flops(c.seq_lens, cfg.q_heads, cfg.head_dim)
+        self.i = 0
+
+    def step(self):
+        import paged_kv_cache_471_amd as da
+        kv = self.kvs[self.i % len(self.kvs)]
+        self.i += 1
+        da.decode_attn_paged(self.q, kv, self.pt, self.sl, self.case.scale, self.out, self.lse,
+                             k_scale=self.ks, v_scale=self.vs)
+
+    @property
+    def batch(self):
+        return len(self.case.seq_lens)
+
+    @property
+    def tokens(self):
+        return int(self.case.seq_lens.astype("int64").sum())
+
+    def oracle_sample(self, budget_s):
+        """Time the float64 oracle on requests in order until the budget is spent."""
+        import numpy as np
+        import oracle
+        from workloads import accounting
+        c, cfg = self.case, self.cfg
+        done = []
+        t0 = time.perf_counter()
+        for b in range(len(c.seq_lens)):
+            oracle.paged_decode_attention(c.q, cfg.q_dtype, c.kv, cfg.kv_dtype, c.page_table, c.seq_lens,
+                                          cfg.page_size, c.scale, c.k_scale, c.v_scale, requests=[b])
+            done.append(b)
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+        lens = c.seq_lens[done]
+        by = accounting.gqa_bytes(lens, cfg.page_size, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.q_dtype,
+                                  cfg.kv_dtype)
+        return dict(seconds=dt, requests=len(done), tokens=int(lens.astype(np.int64).sum()), bytes=by)
+
+
+def _to_dev(x, dtype, dev):
+    import numpy as np
+    import torch
+    import workloads as wl
+    if dtype == wl.F32:
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+    if dtype == wl.BF16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to(dev).view(torch.float8_e4m3fn)
+
+
+def time_runner(runner, steps, warmup, kernel_timer=True):
+    import torch
+    import paged_kv_cache_471_amd as da
+    for _ in range(warmup):
+        runner.step()
+    torch.cuda.synchronize()
+    if kernel_timer:
+        da.timer_begin(steps)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        runner.step()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / steps
+    kms = None
+    if kernel_timer:
+        tot, n = da.timer_end()
+        kms = tot / n if n else None
+    return ms, kms, wall
+
+
+def copy_probe(mb, steps):
+    """Plain device copy of known size (reference for counter scaling and bandwidth)."""
+    import torch
+    n = mb * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    moved = 2 * n * 4
+    print(json.dumps({"mode": "copy", "bytes_read_per_copy": n * 4, "bytes_written_per_copy": n * 4,
+                      "ms_per_copy": ms, "GBps_read_plus_write": moved / ms / 1e6}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama8b")
+    ap.add_argument("--secondary", default="skewed,longfp8",
+                    help="comma list of other workloads to report beside the headline ('' for none)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["bench", "copy", "step"], default="bench",
+                    help="copy: time a plain device copy; step: run the headline step only (for profilers)")
+    ap.add_argument("--copy-mb", type=int, default=1024)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not offered "
+              "(the path shards by request, KV head or sequence; see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import workloads as wl
+    import paged_kv_cache_471_amd as da   # fails loudly if the HIP library is missing
+
+    torch.cuda.set_device(0)
+    if args.mode == "copy":
+        copy_probe(args.copy_mb, args.steps)
+        return
+
+    cfg = wl.CONFIGS[args.workload]
+    runner = GqaRunner(cfg)
+    print(f"# headline {cfg.name}: inputs generated in {runner.gen_s:.1f}s, "
+          f"sum L = {runner.tokens}, {runner.bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
+    if args.mode == "step":
+        ms, kms, _ = time_runner(runner, args.steps, args.warmup, kernel_timer=False)
+        print(json.dumps({"mode": "step", "workload": cfg.name, "ms_per_step": ms}))
+        return
+
+    ms, kms, wall = time_runner(runner, args.steps, args.warmup)
+    headline_case = runner.case
+    gbs = runner.bytes / (ms * 1e-3) / 1e9
+    kern_gbs = runner.bytes / (kms * 1e-3) / 1e9 if kms else None
+    traffic = traffic_from_profiles()
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.DTYPE_NAMES[cfg.kv_dtype],
+        "data": "synthetic",
+        "config": {"workload": workload_desc(cfg), "batch": runner.batch, "q_heads": cfg.q_heads,
+                   "kv_heads": cfg.kv_heads, "head_dim": cfg.head_dim, "page_size": cfg.page_size,
+                   "sum_seq_len": runner.tokens, "seed": cfg.seed},
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": runner.batch / (ms * 1e-3),
+        "kv_tokens_per_s": runner.tokens / (ms * 1e-3),
+        "algorithmic_bytes_per_step": runner.bytes,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gqa_attn_kernel",
+            "achieved": round(kern_gbs, 2) if kern_gbs else None,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(kern_gbs / HBM_PEAK_GBS, 4) if kern_gbs else None,
+            "traffic": traffic,
+            "kernel_ms": kms,
+            "kernel_source_hash": kernel_hash(),
+        },
+    }
+
+    secondary = {}
+    for name in [s for s in args.secondary.split(",") if s]:
+        scfg = wl.CONFIGS[name]
+        if isinstance(scfg, wl.MLAConfig):
+            continue
+        del runner
+        torch.cuda.empty_cache()
+        runner2 = GqaRunner(scfg)
+        sms, skms, _ = time_runner(runner2, max(10, args.steps // 2), max(3, args.warmup // 2))
+        sg = runner2.bytes / (sms * 1e-3) / 1e9
+        secondary[name] = {"workload": workload_desc(scfg), "ms_per_step": sms, "GBps": round(sg, 2),
+                           "pct_hbm_peak": round(100 * sg / HBM_PEAK_GBS, 2),
+                           "kernel_ms": skms,
+                           "kernel_GBps": round(runner2.bytes / (skms * 1e-3) / 1e9, 2) if skms else None,
+                           "decode_tokens_per_s": runner2.batch / (sms * 1e-3),
+                           "kv_tokens_per_s": runner2.tokens / (sms * 1e-3)}
+        runner = runner2
+    if secondary:
+        result["secondary"] = secondary
+
+    if not args.no_cpu_baseline:
+        import threadpoolctl
+        base = GqaRunner.__new__(GqaRunner)
+        base.cfg = cfg
+        base.case = headline_case
+        with threadpoolctl.threadpool_limits(1):
+            s = base.oracle_sample(args.cpu_budget)
+        result["cpu_baseline"] = {
+            "value": round(s["bytes"] / s["seconds"] / 1e9, 4),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"first {s['requests']} of {len(base.case.seq_lens)} requests of {cfg.name} "
+                      f"({s['tokens']} tokens, {s['seconds']:.1f} s), float64 numpy, BLAS limited to 1 thread",
+            "tokens_per_s": s["tokens"] / s["seconds"],
+        }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,213 @@
+/*
+ * decode_attn.h - paged decode attention on AMD MI355X (gfx950), C ABI.
+ *
+ * One call computes one decode step of one attention layer for a batch of
+ * variable-length requests.  Each request brings a single query row per head
+ * and attends over its whole cached history, which lives in fixed-size pages
+ * reached through a per-request page table.
+ *
+ * Sources for the operation (titles of the pages it is defined from):
+ *  - one query token per request, the full KV cache of its context read, a
+ *    memory-bound operator: "OpWeave: Flexible Operator Disaggregation for
+ *    Heterogeneous LLM Serving", App. A.2 (Execution-regime assumptions);
+ *  - every query head attends the complete history, the result defined up to
+ *    floating-point reduction order: "SPLASH: Switching Parallel Layouts of
+ *    Attention with Seamless Handoff for LLM Serving", §3 (Computation);
+ *    a query reads its complete causal prefix, one query row per request in
+ *    decode: SPLASH §4.1 (Handoff) and §4.2;
+ *  - grouped-query heads and the head-shared MLA latent: SPLASH §1 and §2;
+ *    latent width 512 + 64 = 576: "Analytical Provisioning for Attention-FFN
+ *    Disaggregated LLM Serving under Stochastic Workloads", App. B.1;
+ *  - the KV history grows by one appended token per step and is read whole:
+ *    Analytical Provisioning §2 and Fig. 1; paged KV-cache management:
+ *    OpWeave §8; FP8 E4M3 KV with scales: SPLASH App. C.1 and App. B.1.
+ *
+ * Semantics (for request b, query head h, L = seq_lens[b]):
+ *     j = h / (Hq / Hkv)                        (GQA: contiguous head groups)
+ *     s_t = scale * <q[b][h], k_t>,  t < L      (k_t: KV head j's key of token t)
+ *     out[b][h] = sum_t exp(s_t) v_t / sum_t exp(s_t)
+ *     lse[b][h] = ln sum_t exp(s_t)             (natural log, fp32)
+ *     L == 0  ->  out = 0, lse = -inf
+ * Token t lives in physical page page_table[b][t / P], slot t % P.  Slots at
+ * or past L in the last page are never read into the result (they may hold
+ * NaN); page_table entries at or past ceil(L / P) are never read.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers of the current HIP device,
+ *    dense and row-major as documented; descriptors are HOST pointers.
+ *  - The caller owns every buffer; the library never frees or keeps them.
+ *  - Calls are asynchronous and ordered on `stream` (a hipStream_t, NULL for
+ *    the null stream).  Nothing reads device data on the host; there is no
+ *    host synchronisation on the path.
+ *  - Every host-detectable error returns a negative status BEFORE any HIP
+ *    call is made; a HIP launch failure returns DA_ERR_HIP.  Data-dependent
+ *    preconditions (page ids < num_pages, L <= max_pages_per_seq * P,
+ *    L >= 0) are the caller's: the kernels do not check them.
+ *  - Results are bitwise deterministic for identical inputs on one device.
+ *  - The library keeps one workspace per (device, stream), grown with
+ *    hipMalloc the first time a shape needs more; growing synchronises the
+ *    device.  Calls on one stream are ordered; calls on different streams
+ *    use different workspaces.
+ */
+#ifndef DECODE_ATTN_H
+#define DECODE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define DA_OK               0
+#define DA_ERR_NULL        -1   /* a required pointer is NULL */
+#define DA_ERR_SHAPE       -2   /* sizes inconsistent or out of range */
+#define DA_ERR_DTYPE       -3   /* unknown dtype tag, or q/kv combination not offered */
+#define DA_ERR_UNSUPPORTED -4   /* valid request outside what the kernels implement */
+#define DA_ERR_WORKSPACE   -5   /* workspace could not be allocated */
+#define DA_ERR_HIP         -6   /* a HIP call failed; see decode_attn_last_hip_error() */
+
+/* storage dtype tags */
+#define DA_F32       0          /* IEEE binary32 */
+#define DA_BF16      1          /* bfloat16, stored as 16-bit patterns */
+#define DA_FP8_E4M3  2          /* OCP fp8 E4M3FN (bias 7, max 448, no inf) */
+
+/*
+ * Paged GQA / MQA / MHA cache description.
+ *
+ * kv_pages layout: [num_pages][2][num_kv_heads][page_size][head_dim] of
+ * kv_dtype; index 0 of the second axis holds keys, 1 values.  Each
+ * (page, K|V, head) block is page_size * head_dim contiguous elements.
+ * q: [batch][num_q_heads][head_dim] of q_dtype; out: same shape and dtype.
+ * lse: [batch][num_q_heads] fp32.  page_table: int32 [batch][max_pages_per_seq].
+ * seq_lens: int32 [batch].
+ *
+ * Offered: head_dim in {64, 128}; page_size 16; num_q_heads / num_kv_heads in
+ * {1, 2, 4, 8}; (q_dtype, kv_dtype) in {(F32, F32), (BF16, BF16),
+ * (BF16, FP8_E4M3)}.  For fp8, k_scale and v_scale are device fp32
+ * [num_kv_heads]; a stored code x of KV head j means e4m3(x) * scale[j].
+ *
+ * workers / snap_pages: partition knobs, 0 selects the library default (one
+ * worker per resident wavefront; no snapping).  A worker is one wavefront that
+ * processes one contiguous share of all (request, KV head, page) units.
+ */
+typedef struct da_paged_desc {
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t page_size;
+    int32_t num_pages;
+    int32_t max_pages_per_seq;
+    int32_t q_dtype;
+    int32_t kv_dtype;
+    int32_t workers;
+    int32_t snap_pages;
+    const float* k_scale;
+    const float* v_scale;
+} da_paged_desc;
+
+/*
+ * Absorbed MLA cache description: one head-shared bf16 latent of latent_dim
+ * values per token (576 = 512 + 64); every head's key is the whole latent and
+ * its value the first v_dim (512) values.
+ * kv_pages: bf16 [num_pages][page_size][latent_dim]; q: bf16
+ * [batch][num_heads][latent_dim] (already absorbed and roped); out: bf16
+ * [batch][num_heads][v_dim]; lse: fp32 [batch][num_heads].
+ * Offered: latent_dim 576, v_dim 512, page_size 64, num_heads a multiple of 16
+ * up to 128.
+ */
+typedef struct da_mla_desc {
+    int32_t batch;
+    int32_t num_heads;
+    int32_t latent_dim;
+    int32_t v_dim;
+    int32_t page_size;
+    int32_t num_pages;
+    int32_t max_pages_per_seq;
+    int32_t workers;
+    int32_t snap_pages;
+} da_mla_desc;
+
+/*
+ * decode_attn_paged - one decode step of paged grouped-query attention.
+ *   desc        host; shapes and dtypes as above.
+ *   q           device, [B][Hq][D] q_dtype.
+ *   kv_pages    device, [num_pages][2][Hkv][P][D] kv_dtype.
+ *   page_table  device, int32 [B][max_pages_per_seq].
+ *   seq_lens    device, int32 [B]; history length including this step's token.
+ *   scale       multiplies q.k before the (natural) softmax.
+ *   out         device, [B][Hq][D] q_dtype (written).
+ *   lse         device, fp32 [B][Hq] (written), or NULL to skip it.
+ *   stream      hipStream_t.
+ * Returns DA_OK or a negative status.
+ */
+int decode_attn_paged(const da_paged_desc* desc, const void* q, const void* kv_pages,
+                      const int32_t* page_table, const int32_t* seq_lens, float scale,
+                      void* out, float* lse, void* stream);
+
+/*
+ * decode_attn_mla - one decode step of absorbed MLA attention over the
+ * head-shared latent.  Arguments as decode_attn_paged with the MLA layouts.
+ */
+int decode_attn_mla(const da_mla_desc* desc, const void* q, const void* kv_pages,
+                    const int32_t* page_table, const int32_t* seq_lens, float scale,
+                    void* out, float* lse, void* stream);
+
+/*
+ * decode_attn_plan - run the device planner alone (for tests and tools).
+ * The partition of all (request, unit, page) work into `workers` contiguous
+ * shares that the attention kernels use; the integer rule is stated in the
+ * source of the planner.  `units` is the number of KV heads (GQA) or 1 (MLA).
+ * Outputs (device, int32): cp [batch+1] prefix sums of pages per request;
+ * cuts [workers+1]; cursors [workers+1][4] = (request, unit, page, 0) of each
+ * cut's first unit, (batch, 0, 0, 0) for the end; first_worker [batch*units],
+ * -1 for empty streams; split_list [workers] and split_count [1]: the
+ * streams cut into more than one piece, in increasing stream order.
+ * Asynchronous on `stream`.
+ */
+int decode_attn_plan(int32_t batch, const int32_t* seq_lens, int32_t page_size, int32_t units,
+                     int32_t workers, int32_t snap_pages, int32_t max_pages_per_seq,
+                     int32_t* cp, int32_t* cuts, int32_t* cursors, int32_t* first_worker,
+                     int32_t* split_list, int32_t* split_count, void* stream);
+
+/*
+ * paged_kv_gather - copy every live token of the paged cache, through the same
+ * address function the attention kernels use, into a dense array (a bitwise
+ * copy, no arithmetic).  GQA (mla == 0): dense is
+ * [batch][max_pages_per_seq*page_size][2][Hkv][D] of kv_dtype; MLA (mla == 1,
+ * desc fields: num_kv_heads = 1, head_dim = latent_dim): dense is
+ * [batch][max_pages_per_seq*page_size][latent_dim].  Rows t >= L are left
+ * untouched.  Asynchronous on `stream`.
+ */
+int paged_kv_gather(const da_paged_desc* desc, int32_t mla, const void* kv_pages,
+                    const int32_t* page_table, const int32_t* seq_lens, void* dense, void* stream);
+
+/* default number of workers for each path on the current device (host query). */
+int decode_attn_default_workers(const da_paged_desc* gqa_or_null, const da_mla_desc* mla_or_null,
+                                int32_t* workers);
+
+/*
+ * Kernel timer (profiling aid).  decode_attn_timer_begin creates max_launches
+ * start/stop event pairs for the calling thread on the current device; until
+ * decode_attn_timer_end, each decode_attn_* call launches its main attention
+ * kernel with hipExtLaunchKernel and the next pair, so the dispatch itself
+ * records when that kernel starts and ends (no extra packets on the stream).
+ * Calls beyond max_launches are not timed.  decode_attn_timer_end waits for
+ * the recorded events, returns the summed kernel time in milliseconds and the
+ * number of timed launches, and releases the events.
+ */
+int decode_attn_timer_begin(int32_t max_launches);
+int decode_attn_timer_end(double* total_ms, int32_t* launches);
+
+/* human-readable text of a status code (static storage). */
+const char* decode_attn_status_str(int status);
+
+/* the last HIP error code seen by the library on this thread (0 if none). */
+int decode_attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DECODE_ATTN_H */

@@ -1,0 +1,239 @@
+"""Paged GQA / MLA decode attention for AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libdecode_attn.so`` (the C ABI declared in
+``include/decode_attn.h``).  Every step of the computation runs in the HIP
+kernels; this module only turns torch tensors into pointers, shapes and a
+stream.  There is no CPU fallback: if the library is missing, importing the
+binding raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdecode_attn.so")
+
+DA_F32, DA_BF16, DA_FP8_E4M3 = 0, 1, 2
+STATUS = {0: "DA_OK", -1: "DA_ERR_NULL", -2: "DA_ERR_SHAPE", -3: "DA_ERR_DTYPE", -4: "DA_ERR_UNSUPPORTED",
+          -5: "DA_ERR_WORKSPACE", -6: "DA_ERR_HIP"}
+
+EXPORTS = ("decode_attn_paged", "decode_attn_mla", "decode_attn_plan", "paged_kv_gather",
+           "decode_attn_default_workers", "decode_attn_status_str", "decode_attn_last_hip_error",
+           "decode_attn_timer_begin", "decode_attn_timer_end")
+
+
+class PagedDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("max_pages_per_seq", ctypes.c_int32), ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("workers", ctypes.c_int32), ("snap_pages", ctypes.c_int32),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+
+
+class MLADesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("latent_dim", ctypes.c_int32),
+                ("v_dim", ctypes.c_int32), ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("max_pages_per_seq", ctypes.c_int32), ("workers", ctypes.c_int32), ("snap_pages", ctypes.c_int32)]
+
+
+class DecodeAttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        text = _lib.decode_attn_status_str(status).decode() if _lib is not None else ""
+        extra = ""
+        if status == -6 and _lib is not None:
+            extra = f" (hip error {_lib.decode_attn_last_hip_error()})"
+        super().__init__(f"{what}: {STATUS.get(status, status)}: {text}{extra}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python paged_kv_cache_471_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    lib.decode_attn_paged.argtypes = [ctypes.POINTER(PagedDesc), vp, vp, vp, vp, f32, vp, vp, vp]
+    lib.decode_attn_paged.restype = ctypes.c_int
+    lib.decode_attn_mla.argtypes = [ctypes.POINTER(MLADesc), vp, vp, vp, vp, f32, vp, vp, vp]
+    lib.decode_attn_mla.restype = ctypes.c_int
+    lib.decode_attn_plan.argtypes = [i32, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.decode_attn_plan.restype = ctypes.c_int
+    lib.paged_kv_gather.argtypes = [ctypes.POINTER(PagedDesc), i32, vp, vp, vp, vp, vp]
+    lib.paged_kv_gather.restype = ctypes.c_int
+    lib.decode_attn_default_workers.argtypes = [ctypes.POINTER(PagedDesc), ctypes.POINTER(MLADesc),
+                                                ctypes.POINTER(i32)]
+    lib.decode_attn_default_workers.restype = ctypes.c_int
+    lib.decode_attn_status_str.argtypes = [ctypes.c_int]
+    lib.decode_attn_status_str.restype = ctypes.c_char_p
+    lib.decode_attn_last_hip_error.argtypes = []
+    lib.decode_attn_last_hip_error.restype = ctypes.c_int
+    lib.decode_attn_timer_begin.argtypes = [i32]
+    lib.decode_attn_timer_begin.restype = ctypes.c_int
+    lib.decode_attn_timer_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
+    lib.decode_attn_timer_end.restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+# ----------------------------------------------------------------------------- marshalling
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def dtype_tag(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DA_F32
+    if t.dtype == torch.bfloat16:
+        return DA_BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return DA_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise DecodeAttnError(status, what)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("all tensors must be on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("all tensors must be contiguous")
+
+
+def paged_desc(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor, *, k_scale=None, v_scale=None,
+               workers: int = 0, snap_pages: int = 0) -> PagedDesc:
+    B, Hq, D = q.shape
+    num_pages, two, Hkv, P, D2 = kv_pages.shape
+    if two != 2 or D2 != D:
+        raise ValueError(f"kv_pages must be [num_pages][2][Hkv][P][{D}], got {tuple(kv_pages.shape)}")
+    return PagedDesc(B, Hq, Hkv, D, P, num_pages, page_table.shape[1], dtype_tag(q), dtype_tag(kv_pages),
+                     workers, snap_pages, _ptr(k_scale), _ptr(v_scale))
+
+
+def decode_attn_paged(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                      scale: float, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, *,
+                      k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                      workers: int = 0, snap_pages: int = 0, want_lse: bool = True, stream=None):
+    """Paged GQA decode attention.  q [B][Hq][D] (fp32 or bf16); kv_pages
+    [num_pages][2][Hkv][16][D] (fp32, bf16, or fp8-e4m3 as float8_e4m3fn/uint8 with
+    k_scale/v_scale [Hkv] fp32); page_table int32 [B][max_pages]; seq_lens int32 [B].
+    Returns (out [B][Hq][D] in q's dtype, lse [B][Hq] fp32 or None)."""
+    _need_cuda(q, kv_pages, page_table, seq_lens, k_scale, v_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    _need_cuda(out, lse)
+    d = paged_desc(q, kv_pages, page_table, k_scale=k_scale, v_scale=v_scale, workers=workers,
+                   snap_pages=snap_pages)
+    st = _lib.decode_attn_paged(ctypes.byref(d), _ptr(q), _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens),
+                                float(scale), _ptr(out), _ptr(lse), _stream(stream))
+    _check(st, "decode_attn_paged")
+    return out, lse
+
+
+def decode_attn_mla(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                    scale: float, v_dim: int = 512, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, *, workers: int = 0, snap_pages: int = 0,
+                    want_lse: bool = True, stream=None):
+    """Absorbed MLA decode.  q bf16 [B][H][576]; kv_pages bf16 [num_pages][P][576].
+    Returns (out bf16 [B][H][v_dim], lse fp32 [B][H] or None)."""
+    _need_cuda(q, kv_pages, page_table, seq_lens)
+    B, H, Dk = q.shape
+    if out is None:
+        out = torch.empty((B, H, v_dim), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _need_cuda(out, lse)
+    num_pages, P, Dk2 = kv_pages.shape
+    d = MLADesc(B, H, Dk, v_dim, P, num_pages, page_table.shape[1], workers, snap_pages)
+    st = _lib.decode_attn_mla(ctypes.byref(d), _ptr(q), _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens),
+                              float(scale), _ptr(out), _ptr(lse), _stream(stream))
+    _check(st, "decode_attn_mla")
+    return out, lse
+
+
+def decode_attn_plan(seq_lens: torch.Tensor, page_size: int, units: int, workers: int, snap_pages: int,
+                     max_pages_per_seq: int, stream=None):
+    """Run the device planner alone; returns its outputs as int32 tensors."""
+    _need_cuda(seq_lens)
+    B = seq_lens.shape[0]
+    dev = seq_lens.device
+    z = lambda *s: torch.zeros(s, dtype=torch.int32, device=dev)
+    cp, cuts, cursors = z(B + 1), z(workers + 1), z(workers + 1, 4)
+    fw, split_list, split_count = z(B * units), z(max(workers, 1)), z(1)
+    st = _lib.decode_attn_plan(B, _ptr(seq_lens), page_size, units, workers, snap_pages, max_pages_per_seq,
+                               _ptr(cp), _ptr(cuts), _ptr(cursors), _ptr(fw), _ptr(split_list), _ptr(split_count),
+                               _stream(stream))
+    _check(st, "decode_attn_plan")
+    return dict(cp=cp, cuts=cuts, cursors=cursors, first_worker=fw, split_list=split_list,
+                split_count=split_count)
+
+
+def paged_kv_gather(kv_pages: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor, mla: bool = False,
+                    stream=None) -> torch.Tensor:
+    """Dense copy of every live token through the kernels' address function.
+    GQA: [B][max_pages*P][2][Hkv][D]; MLA: [B][max_pages*P][Dk]; rows past L are zero."""
+    _need_cuda(kv_pages, page_table, seq_lens)
+    B, maxp = page_table.shape
+    if mla:
+        num_pages, P, Dk = kv_pages.shape
+        dense = torch.zeros((B, maxp * P, Dk), dtype=kv_pages.dtype, device=kv_pages.device)
+        d = PagedDesc(B, 1, 1, Dk, P, num_pages, maxp, DA_BF16, dtype_tag(kv_pages), 0, 0, None, None)
+    else:
+        num_pages, _, Hkv, P, D = kv_pages.shape
+        dense = torch.zeros((B, maxp * P, 2, Hkv, D), dtype=kv_pages.dtype, device=kv_pages.device)
+        d = PagedDesc(B, Hkv, Hkv, D, P, num_pages, maxp, DA_F32, dtype_tag(kv_pages), 0, 0, None, None)
+    st = _lib.paged_kv_gather(ctypes.byref(d), 1 if mla else 0, _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens),
+                              _ptr(dense), _stream(stream))
+    _check(st, "paged_kv_gather")
+    return dense
+
+
+def default_workers(q: torch.Tensor = None, kv_pages: torch.Tensor = None, page_table: torch.Tensor = None,
+                    *, mla_desc: Optional[MLADesc] = None, k_scale=None, v_scale=None) -> int:
+    out = ctypes.c_int32(0)
+    if mla_desc is not None:
+        st = _lib.decode_attn_default_workers(None, ctypes.byref(mla_desc), ctypes.byref(out))
+    else:
+        d = paged_desc(q, kv_pages, page_table, k_scale=k_scale, v_scale=v_scale)
+        st = _lib.decode_attn_default_workers(ctypes.byref(d), None, ctypes.byref(out))
+    _check(st, "decode_attn_default_workers")
+    return int(out.value)
+
+
+def timer_begin(max_launches: int):
+    """Time the main attention kernel of each following call (see decode_attn.h)."""
+    _check(_lib.decode_attn_timer_begin(int(max_launches)), "decode_attn_timer_begin")
+
+
+def timer_end():
+    """Returns (summed kernel milliseconds, number of timed launches)."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int32(0)
+    _check(_lib.decode_attn_timer_end(ctypes.byref(ms), ctypes.byref(n)), "decode_attn_timer_end")
+    return ms.value, n.value
+
+
+__all__ = ["timer_begin", "timer_end", "decode_attn_paged", "decode_attn_mla", "decode_attn_plan", "paged_kv_gather", "default_workers",
+           "PagedDesc", "MLADesc", "DecodeAttnError", "LIB_PATH", "EXPORTS", "lib"]

@@ -1,0 +1,439 @@
+// C-ABI layer: argument validation, workspace, kernel dispatch.
+//
+// Every check that can be made on the host runs before the first HIP call, so
+// a bad call returns its status without touching the device.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "../../include/decode_attn.h"
+#include "da_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = static_cast<int>(e);
+    return DA_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- workspace
+
+struct Workspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+// Returns a device buffer of at least `bytes` for (current device, stream).
+int get_workspace(hipStream_t stream, size_t bytes, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace& ws = g_ws[{dev, stream}];
+    if (ws.bytes < bytes) {
+        size_t want = round_up(bytes + bytes / 4, 1 << 20);
+        if (ws.ptr != nullptr) {
+            // earlier calls on any stream may still read the old buffer
+            e = hipDeviceSynchronize();
+            if (e != hipSuccess) return hip_fail(e);
+            e = hipFree(ws.ptr);
+            if (e != hipSuccess) return hip_fail(e);
+            ws.ptr = nullptr;
+            ws.bytes = 0;
+        }
+        e = hipMalloc(&ws.ptr, want);
+        if (e != hipSuccess) {
+            g_last_hip_error = static_cast<int>(e);
+            ws.ptr = nullptr;
+            return DA_ERR_WORKSPACE;
+        }
+        ws.bytes = want;
+    }
+    *out = ws.ptr;
+    return DA_OK;
+}
+
+// Carves the planner's and the merge's buffers out of one workspace.
+struct PlanBuffers {
+    int32_t* cp;
+    int32_t* cuts;
+    int4* cursors;
+    int32_t* first_worker;
+    int32_t* split_list;
+    int32_t* split_count;
+    float* o_part;
+    float* lse_part;
+};
+
+size_t layout(int B, int U, int G, int group, int dim, char* base, PlanBuffers* pb) {
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> char* {
+        char* p = base ? base + off : nullptr;
+        off = round_up(off + bytes, 256);
+        return p;
+    };
+    PlanBuffers t;
+    t.cp = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (B + 1)));
+    t.cuts = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (G + 1)));
+    t.cursors = reinterpret_cast<int4*>(take(sizeof(int4) * (G + 1)));
+    t.first_worker = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * static_cast<size_t>(B) * U));
+    t.split_list = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * G));
+    t.split_count = reinterpret_cast<int32_t*>(take(sizeof(int32_t)));
+    t.o_part = reinterpret_cast<float*>(take(sizeof(float) * 2 * static_cast<size_t>(G) * group * dim));
+    t.lse_part = reinterpret_cast<float*>(take(sizeof(float) * 2 * static_cast<size_t>(G) * group));
+    if (pb) *pb = t;
+    return off;
+}
+
+// ---------------------------------------------------------------- kernel timer
+
+struct Timer {
+    bool on = false;
+    size_t next = 0;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+};
+thread_local Timer g_timer;
+
+// Events for the next main-kernel launch of this thread (none if the timer is off or full).
+da::KernelEvents next_kernel_events() {
+    da::KernelEvents k;
+    if (g_timer.on && g_timer.next < g_timer.ev.size()) {
+        k.start = g_timer.ev[g_timer.next].first;
+        k.stop = g_timer.ev[g_timer.next].second;
+        ++g_timer.next;
+    }
+    return k;
+}
+
+void timer_release() {
+    for (auto& p : g_timer.ev) {
+        (void)hipEventDestroy(p.first);
+        (void)hipEventDestroy(p.second);
+    }
+    g_timer.ev.clear();
+    g_timer.next = 0;
+    g_timer.on = false;
+}
+
+// ---------------------------------------------------------------- device facts
+
+struct DeviceInfo {
+    int num_cus = 0;
+};
+std::mutex g_dev_mutex;
+std::map<int, DeviceInfo> g_dev;
+
+int device_cus(int* cus) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    DeviceInfo& d = g_dev[dev];
+    if (d.num_cus == 0) {
+        e = hipDeviceGetAttribute(&d.num_cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    *cus = d.num_cus;
+    return DA_OK;
+}
+
+// ---------------------------------------------------------------- GQA validation
+
+int check_paged(const da_paged_desc* d) {
+    if (d == nullptr) return DA_ERR_NULL;
+    if (d->batch < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->head_dim < 1 || d->page_size < 1 ||
+        d->num_pages < 1 || d->max_pages_per_seq < 1 || d->workers < 0 || d->snap_pages < 0)
+        return DA_ERR_SHAPE;
+    if (d->num_q_heads % d->num_kv_heads != 0) return DA_ERR_SHAPE;
+    const bool qok = d->q_dtype == DA_F32 || d->q_dtype == DA_BF16;
+    const bool kok = d->kv_dtype == DA_F32 || d->kv_dtype == DA_BF16 || d->kv_dtype == DA_FP8_E4M3;
+    if (!qok || !kok) return DA_ERR_DTYPE;
+    const bool combo = (d->q_dtype == DA_F32 && d->kv_dtype == DA_F32) ||
+                       (d->q_dtype == DA_BF16 && d->kv_dtype == DA_BF16) ||
+                       (d->q_dtype == DA_BF16 && d->kv_dtype == DA_FP8_E4M3);
+    if (!combo) return DA_ERR_DTYPE;
+    const int group = d->num_q_heads / d->num_kv_heads;
+    if (d->head_dim != 64 && d->head_dim != 128) return DA_ERR_UNSUPPORTED;
+    if (d->page_size != 16) return DA_ERR_UNSUPPORTED;
+    if (group != 1 && group != 2 && group != 4 && group != 8) return DA_ERR_UNSUPPORTED;
+    if (d->batch > da::kPlanMaxBatch || d->workers > da::kPlanMaxWorkers) return DA_ERR_UNSUPPORTED;
+    const int64_t units_bound = static_cast<int64_t>(d->num_kv_heads) * d->batch * d->max_pages_per_seq;
+    if (units_bound >= (int64_t(1) << 31)) return DA_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(d->max_pages_per_seq) * d->page_size >= (int64_t(1) << 31)) return DA_ERR_SHAPE;
+    if (d->kv_dtype == DA_FP8_E4M3 && (d->k_scale == nullptr || d->v_scale == nullptr)) return DA_ERR_NULL;
+    return DA_OK;
+}
+
+int resolve_gqa_workers(const da_paged_desc* d, int* G) {
+    if (d->workers > 0) {
+        *G = d->workers;
+        return DA_OK;
+    }
+    int cus = 0;
+    int st = device_cus(&cus);
+    if (st != DA_OK) return st;
+    const int group = d->num_q_heads / d->num_kv_heads;
+    const int waves = da::gqa_waves_per_cu(d->q_dtype, d->kv_dtype, d->head_dim, group);
+    if (waves <= 0) return DA_ERR_UNSUPPORTED;
+    int g = cus * waves;
+    if (g > da::kPlanMaxWorkers) g = da::kPlanMaxWorkers;
+    *G = g;
+    return DA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* decode_attn_status_str(int status) {
+    switch (status) {
+        case DA_OK: return "ok";
+        case DA_ERR_NULL: return "a required pointer is NULL";
+        case DA_ERR_SHAPE: return "sizes inconsistent or out of range";
+        case DA_ERR_DTYPE: return "unknown dtype or dtype combination not offered";
+        case DA_ERR_UNSUPPORTED: return "valid request outside what the kernels implement";
+        case DA_ERR_WORKSPACE: return "workspace allocation failed";
+        case DA_ERR_HIP: return "a HIP call failed";
+        default: return "unknown status";
+    }
+}
+
+int decode_attn_last_hip_error(void) { return g_last_hip_error; }
+
+int decode_attn_timer_begin(int32_t max_launches) {
+    if (max_launches < 1 || max_launches > 1000000) return DA_ERR_SHAPE;
+    timer_release();
+    g_timer.ev.reserve(static_cast<size_t>(max_launches));
+    for (int i = 0; i < max_launches; ++i) {
+        hipEvent_t a = nullptr, b = nullptr;
+        hipError_t e = hipEventCreate(&a);
+        if (e == hipSuccess) e = hipEventCreate(&b);
+        if (e != hipSuccess) {
+            if (a) (void)hipEventDestroy(a);
+            timer_release();
+            return hip_fail(e);
+        }
+        g_timer.ev.emplace_back(a, b);
+    }
+    g_timer.on = true;
+    return DA_OK;
+}
+
+int decode_attn_timer_end(double* total_ms, int32_t* launches) {
+    if (total_ms == nullptr || launches == nullptr) return DA_ERR_NULL;
+    double sum = 0.0;
+    int st = DA_OK;
+    for (size_t i = 0; i < g_timer.next; ++i) {
+        hipError_t e = hipEventSynchronize(g_timer.ev[i].second);
+        float ms = 0.0f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, g_timer.ev[i].first, g_timer.ev[i].second);
+        if (e != hipSuccess) {
+            st = hip_fail(e);
+            break;
+        }
+        sum += ms;
+    }
+    *total_ms = sum;
+    *launches = static_cast<int32_t>(g_timer.next);
+    timer_release();
+    return st;
+}
+
+int decode_attn_paged(const da_paged_desc* d, const void* q, const void* kv_pages, const int32_t* page_table,
+                      const int32_t* seq_lens, float scale, void* out, float* lse, void* stream) {
+    int st = check_paged(d);
+    if (st != DA_OK) return st;
+    if (q == nullptr || kv_pages == nullptr || page_table == nullptr || seq_lens == nullptr || out == nullptr)
+        return DA_ERR_NULL;
+    const int elem_q = d->q_dtype == DA_F32 ? 4 : 2;
+    const int elem_kv = d->kv_dtype == DA_F32 ? 4 : (d->kv_dtype == DA_BF16 ? 2 : 1);
+    const size_t lane_bytes = static_cast<size_t>(d->head_dim / 16) * elem_kv;
+    if (!aligned(kv_pages, lane_bytes < 16 ? lane_bytes : 16) || !aligned(q, 8) || !aligned(out, 8) ||
+        !aligned(lse, 4) || !aligned(page_table, 4) || !aligned(seq_lens, 4))
+        return DA_ERR_SHAPE;
+    (void)elem_q;
+    if (!(scale == scale)) return DA_ERR_SHAPE;
+    if (d->batch == 0) return DA_OK;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int G = 0;
+    st = resolve_gqa_workers(d, &G);
+    if (st != DA_OK) return st;
+    const int U = d->num_kv_heads;
+    const int group = d->num_q_heads / d->num_kv_heads;
+    const size_t bytes = layout(d->batch, U, G, group, d->head_dim, nullptr, nullptr);
+    void* ws = nullptr;
+    st = get_workspace(s, bytes, &ws);
+    if (st != DA_OK) return st;
+    PlanBuffers pb;
+    layout(d->batch, U, G, group, d->head_dim, static_cast<char*>(ws), &pb);
+
+    da::PlanArgs pa{};
+    pa.seq_lens = seq_lens;
+    pa.batch = d->batch;
+    pa.page_size = d->page_size;
+    pa.units = U;
+    pa.workers = G;
+    pa.snap = d->snap_pages;
+    pa.cp = pb.cp;
+    pa.cuts = pb.cuts;
+    pa.cursors = pb.cursors;
+    pa.first_worker = pb.first_worker;
+    pa.split_list = pb.split_list;
+    pa.split_count = pb.split_count;
+    pa.out = out;
+    pa.out_elem_bytes = elem_q;
+    pa.lse = lse;
+    pa.heads = d->num_q_heads;
+    pa.out_dim = d->head_dim;
+    hipError_t e = da::launch_plan(pa, s);
+    if (e != hipSuccess) return hip_fail(e);
+
+    da::GqaArgs ga{};
+    ga.q = q;
+    ga.kv = kv_pages;
+    ga.page_table = page_table;
+    ga.seq_lens = seq_lens;
+    ga.k_scale = d->k_scale;
+    ga.v_scale = d->v_scale;
+    ga.scale_log2 = scale * 1.4426950408889634f;
+    ga.batch = d->batch;
+    ga.q_heads = d->num_q_heads;
+    ga.kv_heads = d->num_kv_heads;
+    ga.page_size = d->page_size;
+    ga.max_pages = d->max_pages_per_seq;
+    ga.workers = G;
+    ga.cuts = pb.cuts;
+    ga.cursors = pb.cursors;
+    ga.out = out;
+    ga.lse = lse;
+    ga.o_part = pb.o_part;
+    ga.lse_part = pb.lse_part;
+    e = da::launch_gqa(d->q_dtype, d->kv_dtype, d->head_dim, group, ga, s, next_kernel_events());
+    if (e != hipSuccess) return hip_fail(e);
+
+    da::MergeArgs ma{};
+    ma.seq_lens = seq_lens;
+    ma.batch = d->batch;
+    ma.page_size = d->page_size;
+    ma.units = U;
+    ma.workers = G;
+    ma.group = group;
+    ma.dim = d->head_dim;
+    ma.q_heads = d->num_q_heads;
+    ma.cp = pb.cp;
+    ma.cuts = pb.cuts;
+    ma.first_worker = pb.first_worker;
+    ma.split_list = pb.split_list;
+    ma.split_count = pb.split_count;
+    ma.o_part = pb.o_part;
+    ma.lse_part = pb.lse_part;
+    ma.out = out;
+    ma.out_is_bf16 = d->q_dtype == DA_BF16;
+    ma.lse = lse;
+    int grid = G * group;
+    if (grid > 2048) grid = 2048;
+    e = da::launch_merge(ma, grid, s);
+    if (e != hipSuccess) return hip_fail(e);
+    return DA_OK;
+}
+
+int decode_attn_mla(const da_mla_desc* d, const void* q, const void* kv_pages, const int32_t* page_table,
+                    const int32_t* seq_lens, float scale, void* out, float* lse, void* stream) {
+    (void)d; (void)q; (void)kv_pages; (void)page_table; (void)seq_lens; (void)scale; (void)out; (void)lse;
+    (void)stream;
+    return DA_ERR_UNSUPPORTED;
+}
+
+int decode_attn_plan(int32_t batch, const int32_t* seq_lens, int32_t page_size, int32_t units, int32_t workers,
+                     int32_t snap_pages, int32_t max_pages_per_seq, int32_t* cp, int32_t* cuts, int32_t* cursors,
+                     int32_t* first_worker, int32_t* split_list, int32_t* split_count, void* stream) {
+    if (seq_lens == nullptr || cp == nullptr || cuts == nullptr || cursors == nullptr || first_worker == nullptr ||
+        split_list == nullptr || split_count == nullptr)
+        return DA_ERR_NULL;
+    if (batch < 1 || page_size < 1 || units < 1 || workers < 1 || snap_pages < 0 || max_pages_per_seq < 1)
+        return DA_ERR_SHAPE;
+    if (batch > da::kPlanMaxBatch || workers > da::kPlanMaxWorkers) return DA_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(units) * batch * max_pages_per_seq >= (int64_t(1) << 31)) return DA_ERR_UNSUPPORTED;
+    if (!aligned(cursors, 16)) return DA_ERR_SHAPE;
+    da::PlanArgs pa{};
+    pa.seq_lens = seq_lens;
+    pa.batch = batch;
+    pa.page_size = page_size;
+    pa.units = units;
+    pa.workers = workers;
+    pa.snap = snap_pages;
+    pa.cp = cp;
+    pa.cuts = cuts;
+    pa.cursors = reinterpret_cast<int4*>(cursors);
+    pa.first_worker = first_worker;
+    pa.split_list = split_list;
+    pa.split_count = split_count;
+    pa.out = nullptr;
+    pa.lse = nullptr;
+    hipError_t e = da::launch_plan(pa, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e);
+    return DA_OK;
+}
+
+int paged_kv_gather(const da_paged_desc* d, int32_t mla, const void* kv_pages, const int32_t* page_table,
+                    const int32_t* seq_lens, void* dense, void* stream) {
+    if (d == nullptr || kv_pages == nullptr || page_table == nullptr || seq_lens == nullptr || dense == nullptr)
+        return DA_ERR_NULL;
+    if (d->batch < 1 || d->num_kv_heads < 1 || d->head_dim < 1 || d->page_size < 1 || d->max_pages_per_seq < 1)
+        return DA_ERR_SHAPE;
+    if (mla != 0 && mla != 1) return DA_ERR_SHAPE;
+    if (mla && d->num_kv_heads != 1) return DA_ERR_SHAPE;
+    const int eb = d->kv_dtype == DA_F32 ? 4 : (d->kv_dtype == DA_BF16 ? 2 : (d->kv_dtype == DA_FP8_E4M3 ? 1 : 0));
+    if (eb == 0) return DA_ERR_DTYPE;
+    if ((d->head_dim * eb) % 4 != 0) return DA_ERR_UNSUPPORTED;
+    if (!aligned(kv_pages, 4) || !aligned(dense, 4)) return DA_ERR_SHAPE;
+    if (d->max_pages_per_seq > 65535 || d->batch > 65535) return DA_ERR_UNSUPPORTED;
+    da::GatherArgs ga{};
+    ga.kv = kv_pages;
+    ga.page_table = page_table;
+    ga.seq_lens = seq_lens;
+    ga.dense = dense;
+    ga.batch = d->batch;
+    ga.kv_heads = d->num_kv_heads;
+    ga.head_dim = d->head_dim;
+    ga.page_size = d->page_size;
+    ga.max_pages = d->max_pages_per_seq;
+    ga.elem_bytes = eb;
+    ga.mla = mla;
+    hipError_t e = da::launch_gather(ga, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e);
+    return DA_OK;
+}
+
+int decode_attn_default_workers(const da_paged_desc* gqa, const da_mla_desc* mla, int32_t* workers) {
+    if (workers == nullptr || (gqa == nullptr) == (mla == nullptr)) return DA_ERR_NULL;
+    if (gqa != nullptr) {
+        int st = check_paged(gqa);
+        if (st != DA_OK) return st;
+        int G = 0;
+        da_paged_desc dd = *gqa;
+        dd.workers = 0;
+        st = resolve_gqa_workers(&dd, &G);
+        if (st != DA_OK) return st;
+        *workers = G;
+        return DA_OK;
+    }
+    return DA_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,458 @@
+// Paged GQA decode attention, split-KV worker kernel (gfx950, wave64).
+//
+// What it computes: for one decode step each request contributes one query row
+// per head and reads its whole KV history ("OpWeave: Flexible Operator
+// Disaggregation for Heterogeneous LLM Serving", App. A.2); every head attends
+// the complete history, and a different reduction order is the same result up
+// to rounding ("SPLASH: Switching Parallel Layouts of Attention with Seamless
+// Handoff for LLM Serving", §3, Computation).  Grouped-query heads share one
+// KV head (SPLASH §1).  The step is bandwidth-bound: its time is the KV bytes
+// read over the bandwidth ("Analytical Provisioning for Attention-FFN
+// Disaggregated LLM Serving under Stochastic Workloads", §3.1 and App. B.2.1).
+//
+// Design (one wavefront = one worker of the device partition):
+//  * The worker walks its contiguous share of (request, KV head, page) units.
+//    A page of one KV head is one 16-token block of K and one of V, each
+//    16 * head_dim contiguous elements.
+//  * Lane l covers token rows r = l / 16 (tokens r, r+4, r+8, r+12 of the page)
+//    and the dims [c*D/16, (c+1)*D/16) with c = l % 16, so every load
+//    instruction of the wave reads 4 whole consecutive token rows: contiguous,
+//    16-byte per lane for bf16 at D = 128.
+//  * K and V of the next page are in flight (register double buffer) while the
+//    current page is computed; the page id two units ahead is fetched with a
+//    scalar load.
+//  * q . k partial sums are combined over the 16 lanes of a row with DPP; each
+//    row keeps its own online-softmax state (running max, sum, accumulator) for
+//    the group's query heads, so the softmax needs no cross-row traffic until
+//    the piece ends.  Scores are kept in base 2 with log2(e) folded into the
+//    scale.  All accumulation is fp32; bf16 K uses the bf16 dot2 instruction
+//    (exact products, fp32 sum), fp8 K is converted exactly to bf16 first.
+//  * At the end of a piece the four rows are merged; a piece that is the whole
+//    stream writes out/lse, otherwise (o, log2-sum-exp) goes to a partial slot
+//    that the merge kernel combines.
+#include <hip/hip_ext.h>
+
+#include "da_common.h"
+#include "da_launch.h"
+
+namespace da {
+namespace {
+
+constexpr int kPage = 16;           // tokens per page this kernel is written for
+constexpr int kTPL = kPage / 4;     // tokens per lane per page
+
+template <int QT, int KV, int D, int GS>
+struct Cfg {
+    static constexpr int EB = ElemBytes<KV>::value;
+    static constexpr int DL = D / 16;             // dims per lane
+    static constexpr int NW = DL * EB / 4;        // 32-bit words per lane per token row
+    static constexpr bool kDot = (KV != kF32);    // bf16 pairs + dot2 for q.k
+    static constexpr int QW = kDot ? DL / 2 : DL; // q registers per head
+    static_assert(NW >= 1, "lane slice must be at least one word");
+};
+
+template <int NW>
+struct Words {
+    uint32_t w[NW];
+};
+
+template <int NW>
+__device__ __forceinline__ void load_words(Words<NW>& dst, const char* p) {
+    if constexpr (NW == 1) {
+        dst.w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else if constexpr (NW == 2) {
+        uint2 v = *reinterpret_cast<const uint2*>(p);
+        dst.w[0] = v.x; dst.w[1] = v.y;
+    } else if constexpr (NW == 4) {
+        uint4 v = *reinterpret_cast<const uint4*>(p);
+        dst.w[0] = v.x; dst.w[1] = v.y; dst.w[2] = v.z; dst.w[3] = v.w;
+    } else {
+        static_assert(NW == 8, "unsupported lane slice");
+        uint4 v0 = reinterpret_cast<const uint4*>(p)[0];
+        uint4 v1 = reinterpret_cast<const uint4*>(p)[1];
+        dst.w[0] = v0.x; dst.w[1] = v0.y; dst.w[2] = v0.z; dst.w[3] = v0.w;
+        dst.w[4] = v1.x; dst.w[5] = v1.y; dst.w[6] = v1.z; dst.w[7] = v1.w;
+    }
+}
+
+template <int NW>
+struct PageBuf {
+    Words<NW> k[kTPL];
+    Words<NW> v[kTPL];
+};
+
+// Position of the worker in its share: (request, KV head, page) and the
+// request's length and page count.  All fields are wave-uniform.
+struct Cursor {
+    int b, j, p, len, pages;
+};
+
+__device__ __forceinline__ void cursor_next(Cursor& c, const int32_t* seq_lens, int kv_heads) {
+    if (++c.p < c.pages) return;
+    c.p = 0;
+    if (++c.j < kv_heads) return;
+    c.j = 0;
+    do {
+        ++c.b;
+        c.len = seq_lens[c.b];
+        c.pages = (c.len + kPage - 1) / kPage;
+    } while (c.pages == 0);
+}
+
+template <int QT, int KV, int D, int GS>
+__global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
+    using C = Cfg<QT, KV, D, GS>;
+    constexpr int DL = C::DL, NW = C::NW, QW = C::QW, EB = C::EB;
+
+    const int lane = threadIdx.x & 63;
+    const int row = lane >> 4;            // token row within a group of 4 tokens
+    const int col = lane & 15;            // dim slice
+    const int g = uniform(blockIdx.x * (kGqaBlock / 64) + (threadIdx.x >> 6));
+    if (g >= a.workers) return;
+    const int c0 = a.cuts[g];
+    const int n = a.cuts[g + 1] - c0;
+    if (n <= 0) return;
+
+    const int Hkv = a.kv_heads;
+    const int Hq = a.q_heads;
+    const char* kvb = static_cast<const char*>(a.kv);
+    const int64_t block_elems = static_cast<int64_t>(kPage) * D;   // one (page, K|V, head) block
+    const int lane_off = (row * D + col * DL) * EB;                  // bytes within a 4-row group
+
+    const int4 start = a.cursors[g];
+    Cursor cc;                                 // compute cursor
+    cc.b = start.x; cc.j = start.y; cc.p = start.z;
+    cc.len = a.seq_lens[cc.b];
+    cc.pages = (cc.len + kPage - 1) / kPage;
+    Cursor lc = cc;                            // load cursor (one unit ahead)
+
+    auto page_id = [&](const Cursor& c) -> int {
+        return a.page_table[static_cast<int64_t>(c.b) * a.max_pages + c.p];
+    };
+    auto issue = [&](PageBuf<NW>& buf, int pid, int j) {
+        const char* kbase = kvb + (gqa_kv_offset(pid, 0, j, 0, Hkv, kPage, D)) * EB + lane_off;
+        const char* vbase = kbase + static_cast<int64_t>(Hkv) * block_elems * EB;
+#pragma unroll
+        for (int i = 0; i < kTPL; ++i) load_words<NW>(buf.k[i], kbase + i * 4 * D * EB);
+#pragma unroll
+        for (int i = 0; i < kTPL; ++i) load_words<NW>(buf.v[i], vbase + i * 4 * D * EB);
+    };
+
+    // query registers of the current stream's head group
+    uint32_t qb[GS][QW];
+    float qf[GS][QW];
+    auto load_q = [&](int b, int j) {
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh) {
+            const int64_t base = (static_cast<int64_t>(b) * Hq + j * GS + hh) * D + col * DL;
+            if constexpr (C::kDot) {
+                const uint32_t* src = reinterpret_cast<const uint32_t*>(
+                    static_cast<const uint16_t*>(a.q) + base);
+#pragma unroll
+                for (int w = 0; w < QW; ++w) qb[hh][w] = src[w];
+            } else {
+                const float* src = static_cast<const float*>(a.q) + base;
+#pragma unroll
+                for (int w = 0; w < QW; ++w) qf[hh][w] = src[w];
+            }
+        }
+    };
+
+    float sl2 = a.scale_log2;
+    float vsc = 1.0f;
+    auto stream_scales = [&](int j) {
+        sl2 = a.scale_log2;
+        vsc = 1.0f;
+        if constexpr (KV == kFP8) {
+            sl2 *= a.k_scale[j];
+            vsc = a.v_scale[j];
+        }
+    };
+
+    // online-softmax state of this row
+    float m[GS], l[GS], acc[GS][DL];
+    auto reset = [&]() {
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh) {
+            m[hh] = kMaxInit;
+            l[hh] = 0.0f;
+#pragma unroll
+            for (int d = 0; d < DL; ++d) acc[hh][d] = 0.0f;
+        }
+    };
+
+    auto process = [&](PageBuf<NW>& buf) {
+        const int nvalid = cc.len - cc.p * kPage;   // >= 1
+        const bool tail = nvalid < kPage;
+        float s[GS][kTPL];
+#pragma unroll
+        for (int i = 0; i < kTPL; ++i) {
+            if constexpr (KV == kF32) {
+                float kf[DL];
+#pragma unroll
+                for (int d = 0; d < DL; ++d) kf[d] = __uint_as_float(buf.k[i].w[d]);
+#pragma unroll
+                for (int hh = 0; hh < GS; ++hh) {
+                    float t = 0.0f;
+#pragma unroll
+                    for (int d = 0; d < DL; ++d) t = __builtin_fmaf(qf[hh][d], kf[d], t);
+                    s[hh][i] = t;
+                }
+            } else {
+                uint32_t kp[QW];     // bf16 pairs of this lane's slice of the key
+                if constexpr (KV == kBF16) {
+#pragma unroll
+                    for (int w = 0; w < QW; ++w) kp[w] = buf.k[i].w[w];
+                } else {
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) {
+                        kp[2 * w] = fp8x2_to_bf16x2<false>(buf.k[i].w[w]);
+                        kp[2 * w + 1] = fp8x2_to_bf16x2<true>(buf.k[i].w[w]);
+                    }
+                }
+#pragma unroll
+                for (int hh = 0; hh < GS; ++hh) {
+                    float t = 0.0f;
+#pragma unroll
+                    for (int w = 0; w < QW; ++w) t = dot2_bf16(qb[hh][w], kp[w], t);
+                    s[hh][i] = t;
+                }
+            }
+        }
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh)
+#pragma unroll
+            for (int i = 0; i < kTPL; ++i) s[hh][i] = row16_sum(s[hh][i]) * sl2;
+        if (tail) {
+#pragma unroll
+            for (int i = 0; i < kTPL; ++i) {
+                if (i * 4 + row >= nvalid) {
+#pragma unroll
+                    for (int hh = 0; hh < GS; ++hh) s[hh][i] = -__builtin_inff();
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) buf.v[i].w[w] = 0u;
+                }
+            }
+        }
+        float p[GS][kTPL];
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh) {
+            float mx = s[hh][0];
+#pragma unroll
+            for (int i = 1; i < kTPL; ++i) mx = fmaxf(mx, s[hh][i]);
+            const float mn = fmaxf(m[hh], mx);
+            const float alpha = __builtin_amdgcn_exp2f(m[hh] - mn);
+#pragma unroll
+            for (int i = 0; i < kTPL; ++i) p[hh][i] = __builtin_amdgcn_exp2f(s[hh][i] - mn);
+            float sum = p[hh][0];
+#pragma unroll
+            for (int i = 1; i < kTPL; ++i) sum += p[hh][i];
+            m[hh] = mn;
+            l[hh] = __builtin_fmaf(l[hh], alpha, sum);
+#pragma unroll
+            for (int d = 0; d < DL; ++d) acc[hh][d] *= alpha;
+        }
+#pragma unroll
+        for (int i = 0; i < kTPL; ++i) {
+            float vf[DL];
+            if constexpr (KV == kF32) {
+#pragma unroll
+                for (int d = 0; d < DL; ++d) vf[d] = __uint_as_float(buf.v[i].w[d]);
+            } else if constexpr (KV == kBF16) {
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    vf[2 * w] = bf16_lo(buf.v[i].w[w]);
+                    vf[2 * w + 1] = bf16_hi(buf.v[i].w[w]);
+                }
+            } else {
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    floatx2_t lo = fp8x2_to_f32x2<false>(buf.v[i].w[w]);
+                    floatx2_t hi = fp8x2_to_f32x2<true>(buf.v[i].w[w]);
+                    vf[4 * w] = lo.x; vf[4 * w + 1] = lo.y;
+                    vf[4 * w + 2] = hi.x; vf[4 * w + 3] = hi.y;
+                }
+            }
+#pragma unroll
+            for (int hh = 0; hh < GS; ++hh)
+#pragma unroll
+                for (int d = 0; d < DL; ++d) acc[hh][d] = __builtin_fmaf(p[hh][i], vf[d], acc[hh][d]);
+        }
+    };
+
+    // merge the four rows and write the piece's result
+    auto finalize = [&](bool whole, int slot) {
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh) {
+#pragma unroll
+            for (int x = 16; x <= 32; x <<= 1) {
+                const float mo = shfl_xor_f(m[hh], x);
+                const float lo = shfl_xor_f(l[hh], x);
+                const float mm = fmaxf(m[hh], mo);
+                const float fs = __builtin_amdgcn_exp2f(m[hh] - mm);
+                const float fo = __builtin_amdgcn_exp2f(mo - mm);
+                l[hh] = l[hh] * fs + lo * fo;
+#pragma unroll
+                for (int d = 0; d < DL; ++d) {
+                    const float ao = shfl_xor_f(acc[hh][d], x);
+                    acc[hh][d] = acc[hh][d] * fs + ao * fo;
+                }
+                m[hh] = mm;
+            }
+        }
+#pragma unroll
+        for (int hh = 0; hh < GS; ++hh) {
+            if ((hh & 3) != row) continue;
+            const float inv = vsc / l[hh];
+            const float lse2 = m[hh] + __builtin_log2f(l[hh]);
+            if (whole) {
+                const int64_t o = (static_cast<int64_t>(cc.b) * Hq + cc.j * GS + hh) * D + col * DL;
+                if constexpr (QT == kF32) {
+                    float* dst = static_cast<float*>(a.out) + o;
+#pragma unroll
+                    for (int d = 0; d < DL; ++d) dst[d] = acc[hh][d] * inv;
+                } else {
+                    uint32_t packed[DL / 2];
+#pragma unroll
+                    for (int d = 0; d < DL / 2; ++d) {
+                        const uint32_t lo16 = f32_to_bf16_bits(acc[hh][2 * d] * inv);
+                        const uint32_t hi16 = f32_to_bf16_bits(acc[hh][2 * d + 1] * inv);
+                        packed[d] = lo16 | (hi16 << 16);
+                    }
+                    uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + o);
+#pragma unroll
+                    for (int d = 0; d < DL / 2; ++d) dst[d] = packed[d];
+                }
+                if (col == 0 && a.lse != nullptr)
+                    a.lse[static_cast<int64_t>(cc.b) * Hq + cc.j * GS + hh] = lse2 * kLn2;
+            } else {
+                float* dst = a.o_part + (static_cast<int64_t>(slot) * GS + hh) * D + col * DL;
+#pragma unroll
+                for (int d = 0; d < DL; ++d) dst[d] = acc[hh][d] * inv;
+                if (col == 0) a.lse_part[static_cast<int64_t>(slot) * GS + hh] = lse2;
+            }
+        }
+    };
+
+    // ---- prologue
+    load_q(cc.b, cc.j);
+    stream_scales(cc.j);
+    reset();
+    bool first_piece = true;
+    int piece_p0 = cc.p;
+
+    PageBuf<NW> A, Bf;
+    int pid = page_id(lc);
+    issue(A, pid, lc.j);
+    if (n > 1) {
+        cursor_next(lc, a.seq_lens, Hkv);
+        pid = page_id(lc);
+    }
+
+    // after computing unit k: close the piece if the stream or the share ends
+    auto end_of_unit = [&](int k) {
+        const bool stream_end = (cc.p == cc.pages - 1);
+        const bool share_end = (k == n - 1);
+        if (stream_end || share_end) {
+            finalize(stream_end && piece_p0 == 0, first_piece ? g : a.workers + g);
+            if (!share_end) {
+                cursor_next(cc, a.seq_lens, Hkv);
+                first_piece = false;
+                piece_p0 = 0;
+                load_q(cc.b, cc.j);
+                stream_scales(cc.j);
+                reset();
+            }
+        } else {
+            ++cc.p;
+        }
+    };
+
+    for (int k = 0; k < n;) {
+        if (k + 1 < n) {
+            issue(Bf, pid, lc.j);
+            if (k + 2 < n) {
+                cursor_next(lc, a.seq_lens, Hkv);
+                pid = page_id(lc);
+            }
+        }
+        process(A);
+        end_of_unit(k);
+        if (++k >= n) break;
+        if (k + 1 < n) {
+            issue(A, pid, lc.j);
+            if (k + 2 < n) {
+                cursor_next(lc, a.seq_lens, Hkv);
+                pid = page_id(lc);
+            }
+        }
+        process(Bf);
+        end_of_unit(k);
+        ++k;
+    }
+}
+
+template <int QT, int KV, int D, int GS>
+hipError_t launch_one(const GqaArgs& a, hipStream_t s, const KernelEvents& ev) {
+    const int per_block = kGqaBlock / 64;
+    const int grid = (a.workers + per_block - 1) / per_block;
+    if (ev.start != nullptr)
+        hipExtLaunchKernelGGL((gqa_attn_kernel<QT, KV, D, GS>), dim3(grid), dim3(kGqaBlock), 0, s, ev.start,
+                              ev.stop, 0, a);
+    else
+        hipLaunchKernelGGL((gqa_attn_kernel<QT, KV, D, GS>), dim3(grid), dim3(kGqaBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int QT, int KV, int D, int GS>
+int waves_one() {
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, gqa_attn_kernel<QT, KV, D, GS>, kGqaBlock, 0) !=
+        hipSuccess)
+        return 0;
+    return blocks * (kGqaBlock / 64);
+}
+
+template <int QT, int KV, int D>
+hipError_t by_group(int group, const GqaArgs* a, hipStream_t s, const KernelEvents& ev, int* waves) {
+    switch (group) {
+        case 1: if (waves) { *waves = waves_one<QT, KV, D, 1>(); return hipSuccess; } return launch_one<QT, KV, D, 1>(*a, s, ev);
+        case 2: if (waves) { *waves = waves_one<QT, KV, D, 2>(); return hipSuccess; } return launch_one<QT, KV, D, 2>(*a, s, ev);
+        case 4: if (waves) { *waves = waves_one<QT, KV, D, 4>(); return hipSuccess; } return launch_one<QT, KV, D, 4>(*a, s, ev);
+        case 8: if (waves) { *waves = waves_one<QT, KV, D, 8>(); return hipSuccess; } return launch_one<QT, KV, D, 8>(*a, s, ev);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int QT, int KV>
+hipError_t by_dim(int dim, int group, const GqaArgs* a, hipStream_t s, const KernelEvents& ev, int* waves) {
+    switch (dim) {
+        case 64: return by_group<QT, KV, 64>(group, a, s, ev, waves);
+        case 128: return by_group<QT, KV, 128>(group, a, s, ev, waves);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t dispatch(int q_dtype, int kv_dtype, int dim, int group, const GqaArgs* a, hipStream_t s,
+                    const KernelEvents& ev, int* waves) {
+    if (q_dtype == kF32 && kv_dtype == kF32) return by_dim<kF32, kF32>(dim, group, a, s, ev, waves);
+    if (q_dtype == kBF16 && kv_dtype == kBF16) return by_dim<kBF16, kBF16>(dim, group, a, s, ev, waves);
+    if (q_dtype == kBF16 && kv_dtype == kFP8) return by_dim<kBF16, kFP8>(dim, group, a, s, ev, waves);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_gqa(int q_dtype, int kv_dtype, int head_dim, int group, const GqaArgs& a, hipStream_t s,
+                      const KernelEvents& ev) {
+    return dispatch(q_dtype, kv_dtype, head_dim, group, &a, s, ev, nullptr);
+}
+
+int gqa_waves_per_cu(int q_dtype, int kv_dtype, int head_dim, int group) {
+    int waves = 0;
+    if (dispatch(q_dtype, kv_dtype, head_dim, group, nullptr, nullptr, KernelEvents{}, &waves) != hipSuccess)
+        return 0;
+    return waves;
+}
+
+}  // namespace da
