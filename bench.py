@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attention KV GB/s (% of HBM peak) + tokens/s per step, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK = 2.5e15         # dense bf16 FLOP/s, MI355X
 KERNEL_SOURCES = ["paged_kv_cache_471_amd/csrc/gqa.hip", "paged_kv_cache_471_amd/csrc/da_common.h",
                   "paged_kv_cache_471_amd/csrc/da_launch.h"]
 PMC_FILE = os.path.join(ROOT, "profiles", "gqa_llama8b_pmc.md")
@@ -130,6 +131,49 @@ class GqaRunner:
         return dict(seconds=dt, requests=len(done), tokens=int(lens.astype(np.int64).sum()), bytes=by)
 
 
+class MlaRunner:
+    def __init__(self, cfg, sets=2):
+        import torch
+        import workloads as wl
+        from workloads import accounting
+        self.cfg = cfg
+        t0 = time.time()
+        self.case = wl.make_mla_case(cfg)
+        self.gen_s = time.time() - t0
+        c = self.case
+        dev = "cuda"
+        self.q = _to_dev(c.q, wl.BF16, dev)
+        kv0 = _to_dev(c.kv, wl.BF16, dev)
+        self.kvs = [kv0] + [kv0.clone() for _ in range(sets - 1)]
+        self.pt = torch.from_numpy(c.page_table).to(dev)
+        self.sl = torch.from_numpy(c.seq_lens).to(dev)
+        B, H = c.q.shape[:2]
+        self.out = torch.empty((B, H, cfg.v_dim), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+        self.bytes = accounting.mla_bytes(c.seq_lens, cfg.page_size, H, cfg.latent_dim, cfg.v_dim)
+        self.flops = accounting.mla_flops(c.seq_lens, H, cfg.latent_dim, cfg.v_dim)
+        self.i = 0
+
+    def step(self):
+        import paged_kv_cache_471_amd as da
+        kv = self.kvs[self.i % len(self.kvs)]
+        self.i += 1
+        da.decode_attn_mla(self.q, kv, self.pt, self.sl, self.case.scale, self.cfg.v_dim, self.out, self.lse)
+
+    @property
+    def batch(self):
+        return len(self.case.seq_lens)
+
+    @property
+    def tokens(self):
+        return int(self.case.seq_lens.astype("int64").sum())
+
+
+def make_runner(cfg):
+    import workloads as wl
+    return MlaRunner(cfg) if isinstance(cfg, wl.MLAConfig) else GqaRunner(cfg)
+
+
 def _to_dev(x, dtype, dev):
     import numpy as np
     import torch
@@ -194,7 +238,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b")
-    ap.add_argument("--secondary", default="skewed,longfp8",
+    ap.add_argument("--secondary", default="skewed,mla,longfp8",
                     help="comma list of other workloads to report beside the headline ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -219,7 +263,7 @@ def main():
         return
 
     cfg = wl.CONFIGS[args.workload]
-    runner = GqaRunner(cfg)
+    runner = make_runner(cfg)
     print(f"# headline {cfg.name}: inputs generated in {runner.gen_s:.1f}s, "
           f"sum L = {runner.tokens}, {runner.bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
     if args.mode == "step":
@@ -269,19 +313,25 @@ def main():
     secondary = {}
     for name in [s for s in args.secondary.split(",") if s]:
         scfg = wl.CONFIGS[name]
-        if isinstance(scfg, wl.MLAConfig):
-            continue
         del runner
         torch.cuda.empty_cache()
-        runner2 = GqaRunner(scfg)
+        runner2 = make_runner(scfg)
+        print(f"# secondary {name}: sum L = {runner2.tokens}, {runner2.bytes / 1e6:.1f} MB", file=sys.stderr,
+              flush=True)
         sms, skms, _ = time_runner(runner2, max(10, args.steps // 2), max(3, args.warmup // 2))
         sg = runner2.bytes / (sms * 1e-3) / 1e9
-        secondary[name] = {"workload": workload_desc(scfg), "ms_per_step": sms, "GBps": round(sg, 2),
-                           "pct_hbm_peak": round(100 * sg / HBM_PEAK_GBS, 2),
-                           "kernel_ms": skms,
-                           "kernel_GBps": round(runner2.bytes / (skms * 1e-3) / 1e9, 2) if skms else None,
-                           "decode_tokens_per_s": runner2.batch / (sms * 1e-3),
-                           "kv_tokens_per_s": runner2.tokens / (sms * 1e-3)}
+        entry = {"workload": workload_desc(scfg), "ms_per_step": sms, "GBps": round(sg, 2),
+                 "pct_hbm_peak": round(100 * sg / HBM_PEAK_GBS, 2),
+                 "kernel_ms": skms,
+                 "kernel_GBps": round(runner2.bytes / (skms * 1e-3) / 1e9, 2) if skms else None,
+                 "decode_tokens_per_s": runner2.batch / (sms * 1e-3),
+                 "kv_tokens_per_s": runner2.tokens / (sms * 1e-3),
+                 "algorithmic_bytes_per_step": runner2.bytes}
+        if isinstance(scfg, wl.MLAConfig):
+            entry["algorithmic_flops_per_step"] = runner2.flops
+            entry["mfma_TFLOPs"] = round(runner2.flops / (sms * 1e-3) / 1e12, 1)
+            entry["pct_mfma_bf16_peak"] = round(100 * runner2.flops / (sms * 1e-3) / MFMA_BF16_PEAK, 2)
+        secondary[name] = entry
         runner = runner2
     if secondary:
         result["secondary"] = secondary

@@ -88,9 +88,10 @@ extern "C" {
  * (BF16, FP8_E4M3)}.  For fp8, k_scale and v_scale are device fp32
  * [num_kv_heads]; a stored code x of KV head j means e4m3(x) * scale[j].
  *
- * workers / snap_pages: partition knobs, 0 selects the library default (one
- * worker per resident wavefront; no snapping).  A worker is one wavefront that
- * processes one contiguous share of all (request, KV head, page) units.
+ * workers: number of workers, 0 selects the library default (one per resident
+ * wavefront).  A worker is one wavefront that processes one contiguous share
+ * of all (request, KV head, page) units; see decode_attn_plan for the rule.
+ * Limits: batch <= 8192, workers <= 16384.
  */
 typedef struct da_paged_desc {
     int32_t batch;
@@ -103,7 +104,6 @@ typedef struct da_paged_desc {
     int32_t q_dtype;
     int32_t kv_dtype;
     int32_t workers;
-    int32_t snap_pages;
     const float* k_scale;
     const float* v_scale;
 } da_paged_desc;
@@ -115,8 +115,10 @@ typedef struct da_paged_desc {
  * kv_pages: bf16 [num_pages][page_size][latent_dim]; q: bf16
  * [batch][num_heads][latent_dim] (already absorbed and roped); out: bf16
  * [batch][num_heads][v_dim]; lse: fp32 [batch][num_heads].
- * Offered: latent_dim 576, v_dim 512, page_size 64, num_heads a multiple of 16
- * up to 128.
+ * Offered: latent_dim 576, v_dim 512, page_size a multiple of 32 up to 256,
+ * num_heads in {16, 32, 64, 128}.  workers: number of workgroups (0 = one per
+ * compute unit); each processes one contiguous share of all (request, page)
+ * units.  Limits: batch <= 8192, workers <= 2048.
  */
 typedef struct da_mla_desc {
     int32_t batch;
@@ -127,7 +129,6 @@ typedef struct da_mla_desc {
     int32_t num_pages;
     int32_t max_pages_per_seq;
     int32_t workers;
-    int32_t snap_pages;
 } da_mla_desc;
 
 /*
@@ -156,21 +157,30 @@ int decode_attn_mla(const da_mla_desc* desc, const void* q, const void* kv_pages
                     void* out, float* lse, void* stream);
 
 /*
- * decode_attn_plan - run the device planner alone (for tests and tools).
- * The partition of all (request, unit, page) work into `workers` contiguous
- * shares that the attention kernels use; the integer rule is stated in the
- * source of the planner.  `units` is the number of KV heads (GQA) or 1 (MLA).
- * Outputs (device, int32): cp [batch+1] prefix sums of pages per request;
- * cuts [workers+1]; cursors [workers+1][4] = (request, unit, page, 0) of each
- * cut's first unit, (batch, 0, 0, 0) for the end; first_worker [batch*units],
- * -1 for empty streams; split_list [workers] and split_count [1]: the
- * streams cut into more than one piece, in increasing stream order.
- * Asynchronous on `stream`.
+ * decode_attn_plan - run the split-KV planner that the attention kernels
+ * execute in-kernel, alone, and write what it decides (for tests and tools).
+ * The rule: stream (b, j), j < units, owns ceil(seq_lens[b] / page_size) page
+ * units; streams are ordered b-major; W is the total; A = min(workers, W)
+ * workers are active and worker g < A takes units [floor(g*W/A),
+ * floor((g+1)*W/A)).  The step ends with its slowest worker, so the largest
+ * share is what the rule minimises ("Analytical Provisioning for Attention-FFN
+ * Disaggregated LLM Serving under Stochastic Workloads", §3.3).
+ *   units        number of KV heads (GQA) or 1 (MLA).
+ *   active       device int32 [1]: A.
+ *   cuts         device int32 [workers + 1]: the first unit of each worker,
+ *                W for g >= A.
+ *   cursors      device int32 [workers + 1][4]: (request, unit, page, 0) of
+ *                each cut, (batch, 0, 0, 0) where the cut is W.
+ *   first_worker device int32 [batch * units]: worker holding the first piece
+ *                of each stream, -1 for empty streams.
+ *   piece_count  device int32 [batch * units]: number of workers the stream
+ *                is split over (0 for empty streams).
+ * Asynchronous on `stream`.  Returns DA_ERR_NULL / DA_ERR_SHAPE /
+ * DA_ERR_UNSUPPORTED (batch > 8192, workers > 16384) before any launch.
  */
 int decode_attn_plan(int32_t batch, const int32_t* seq_lens, int32_t page_size, int32_t units,
-                     int32_t workers, int32_t snap_pages, int32_t max_pages_per_seq,
-                     int32_t* cp, int32_t* cuts, int32_t* cursors, int32_t* first_worker,
-                     int32_t* split_list, int32_t* split_count, void* stream);
+                     int32_t workers, int32_t* active, int32_t* cuts, int32_t* cursors,
+                     int32_t* first_worker, int32_t* piece_count, void* stream);
 
 /*
  * paged_kv_gather - copy every live token of the paged cache, through the same

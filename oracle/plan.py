@@ -6,7 +6,7 @@ with its slowest worker, so the load that matters is the maximum over workers
 the per-worker token loads), and attention time grows linearly with the token
 load (same paper, §3.1).  The partition below is this library's own integer
 rule for making that maximum as small as possible on one GPU: cut the step's
-total page work into G equal contiguous shares, one per worker.  It is pinned
+total page work into equal contiguous shares, one per worker.  It is pinned
 bit-for-bit against the device planner.
 
 Definitions (all integers):
@@ -17,21 +17,23 @@ Definitions (all integers):
 * cp = exclusive prefix sum of pages_b (B + 1 entries); stream (b, j) covers
   units [start, end) with start = U * cp[b] + j * pages_b, end = start + pages_b.
   W = U * cp[B] units in total.
-* Raw cut points c_g = floor(g * W / G) for g = 0..G.
-* Snapping (snap >= 0 units): a cut strictly inside a stream, with d_lo = c -
-  start and d_hi = end - c, moves to start if d_lo <= d_hi and d_lo <= snap, or
-  to end if d_hi < d_lo and d_hi <= snap.  snap = 0 leaves every cut alone.
-  Snapping is monotone, so the cuts stay sorted.
-* Worker g processes units [c_g, c_{g+1}).  The cursor of unit w < W is
-  (b, j, p) with start(b, j) + p = w; the cursor of W is (B, 0, 0).
+* A = min(G, W) workers are active (G launched); the others have no share.
+* Cut points c_g = floor(g * W / A) for g = 0..A; worker g < A processes
+  units [c_g, c_{g+1}), never an empty range because W >= A.
+* The cursor of unit w < W is (b, j, p) with start(b, j) + p = w; the cursor
+  of W is (B, 0, 0).
 * A piece is the part of one stream inside one worker's range.  Its result is
   final when the piece is the whole stream; otherwise it is a partial stored in
   slot g when the piece begins at c_g (the worker's first piece) and in slot
-  G + g otherwise (then it is the worker's last piece).  2G slots suffice.
-* first_worker of a non-empty stream is the largest g with c_g <= start; the
-  stream's pieces, in token order, come from first_worker and then from every
-  later worker g with a non-empty range and c_g < end.  Empty streams (L_b = 0)
-  have first_worker = -1.
+  A + g otherwise (then it is the worker's last piece).  2A slots suffice.
+* The pieces of a non-empty stream come from the consecutive workers
+  first_worker .. first_worker + piece_count - 1 in token order; first_worker
+  is the largest g with c_g <= start.  Empty streams (L_b = 0) have
+  first_worker = -1 and piece_count = 0.
+
+Here every quantity is found by direct search and enumeration; the device
+derives first_worker and piece_count in closed form from (start, end, W, A),
+which the GPU tests compare with these values.
 """
 from __future__ import annotations
 
@@ -45,9 +47,11 @@ import numpy as np
 class Partition:
     cp: np.ndarray            # int64 [B+1]
     total: int                # W
-    cuts: np.ndarray          # int64 [G+1]
-    cursors: np.ndarray       # int64 [G+1][3] (b, j, p) of unit cuts[g]
+    active: int               # A = min(G, W)
+    cuts: np.ndarray          # int64 [A+1]
+    cursors: np.ndarray       # int64 [A+1][3] (b, j, p) of unit cuts[g]
     first_worker: np.ndarray  # int64 [B*U]
+    piece_count: np.ndarray   # int64 [B*U]
     pieces: List[Tuple[int, int, int, int, int, int]]   # (g, b, j, p0, p1, slot)
 
 
@@ -59,7 +63,7 @@ def _stream_of(w: int, cp: np.ndarray, U: int, B: int):
     return b, off // pages, off % pages
 
 
-def partition(seq_lens, page_size: int, units: int, workers: int, snap: int = 0) -> Partition:
+def partition(seq_lens, page_size: int, units: int, workers: int) -> Partition:
     L = np.asarray(seq_lens, dtype=np.int64)
     B = len(L)
     U = int(units)
@@ -68,39 +72,17 @@ def partition(seq_lens, page_size: int, units: int, workers: int, snap: int = 0)
     cp = np.zeros(B + 1, dtype=np.int64)
     cp[1:] = np.cumsum(pages)
     W = U * int(cp[B])
+    A = min(G, W)
 
-    cuts = np.array([(g * W) // G for g in range(G + 1)], dtype=np.int64)
-    if snap > 0:
-        for g in range(1, G):
-            c = int(cuts[g])
-            if c >= W:
-                continue
-            b, j, p = _stream_of(c, cp, U, B)
-            start = U * int(cp[b]) + j * int(pages[b])
-            end = start + int(pages[b])
-            d_lo, d_hi = c - start, end - c
-            if d_lo == 0:
-                continue
-            if d_lo <= d_hi and d_lo <= snap:
-                cuts[g] = start
-            elif d_hi < d_lo and d_hi <= snap:
-                cuts[g] = end
+    cuts = np.array([(g * W) // A for g in range(A + 1)] if A else [0], dtype=np.int64)
 
-    cursors = np.zeros((G + 1, 3), dtype=np.int64)
-    for g in range(G + 1):
+    cursors = np.zeros((A + 1, 3), dtype=np.int64)
+    for g in range(A + 1):
         c = int(cuts[g])
         cursors[g] = (B, 0, 0) if c >= W else _stream_of(c, cp, U, B)
 
-    first_worker = np.full(B * U, -1, dtype=np.int64)
-    for b in range(B):
-        if pages[b] == 0:
-            continue
-        for j in range(U):
-            start = U * int(cp[b]) + j * int(pages[b])
-            first_worker[b * U + j] = int(np.searchsorted(cuts, start, side="right")) - 1
-
     pieces = []
-    for g in range(G):
+    for g in range(A):
         lo, hi = int(cuts[g]), int(cuts[g + 1])
         w = lo
         while w < hi:
@@ -114,7 +96,15 @@ def partition(seq_lens, page_size: int, units: int, workers: int, snap: int = 0)
             elif w == lo:
                 slot = g
             else:
-                slot = G + g
+                slot = A + g
             pieces.append((g, b, j, p0, p1, slot))
             w = stop
-    return Partition(cp, W, cuts, cursors, first_worker, pieces)
+
+    first_worker = np.full(B * U, -1, dtype=np.int64)
+    piece_count = np.zeros(B * U, dtype=np.int64)
+    for g, b, j, p0, p1, slot in pieces:
+        s = b * U + j
+        if first_worker[s] < 0:
+            first_worker[s] = g
+        piece_count[s] += 1
+    return Partition(cp, W, A, cuts, cursors, first_worker, piece_count, pieces)

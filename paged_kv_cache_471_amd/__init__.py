@@ -30,14 +30,13 @@ class PagedDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
                 ("max_pages_per_seq", ctypes.c_int32), ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-                ("workers", ctypes.c_int32), ("snap_pages", ctypes.c_int32),
-                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+                ("workers", ctypes.c_int32), ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
 class MLADesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("latent_dim", ctypes.c_int32),
                 ("v_dim", ctypes.c_int32), ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
-                ("max_pages_per_seq", ctypes.c_int32), ("workers", ctypes.c_int32), ("snap_pages", ctypes.c_int32)]
+                ("max_pages_per_seq", ctypes.c_int32), ("workers", ctypes.c_int32)]
 
 
 class DecodeAttnError(RuntimeError):
@@ -59,7 +58,7 @@ def _load():
     lib.decode_attn_paged.restype = ctypes.c_int
     lib.decode_attn_mla.argtypes = [ctypes.POINTER(MLADesc), vp, vp, vp, vp, f32, vp, vp, vp]
     lib.decode_attn_mla.restype = ctypes.c_int
-    lib.decode_attn_plan.argtypes = [i32, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.decode_attn_plan.argtypes = [i32, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
     lib.decode_attn_plan.restype = ctypes.c_int
     lib.paged_kv_gather.argtypes = [ctypes.POINTER(PagedDesc), i32, vp, vp, vp, vp, vp]
     lib.paged_kv_gather.restype = ctypes.c_int
@@ -121,19 +120,19 @@ def _need_cuda(*ts):
 
 
 def paged_desc(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor, *, k_scale=None, v_scale=None,
-               workers: int = 0, snap_pages: int = 0) -> PagedDesc:
+               workers: int = 0) -> PagedDesc:
     B, Hq, D = q.shape
     num_pages, two, Hkv, P, D2 = kv_pages.shape
     if two != 2 or D2 != D:
         raise ValueError(f"kv_pages must be [num_pages][2][Hkv][P][{D}], got {tuple(kv_pages.shape)}")
     return PagedDesc(B, Hq, Hkv, D, P, num_pages, page_table.shape[1], dtype_tag(q), dtype_tag(kv_pages),
-                     workers, snap_pages, _ptr(k_scale), _ptr(v_scale))
+                     workers, _ptr(k_scale), _ptr(v_scale))
 
 
 def decode_attn_paged(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
                       scale: float, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, *,
                       k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
-                      workers: int = 0, snap_pages: int = 0, want_lse: bool = True, stream=None):
+                      workers: int = 0, want_lse: bool = True, stream=None):
     """Paged GQA decode attention.  q [B][Hq][D] (fp32 or bf16); kv_pages
     [num_pages][2][Hkv][16][D] (fp32, bf16, or fp8-e4m3 as float8_e4m3fn/uint8 with
     k_scale/v_scale [Hkv] fp32); page_table int32 [B][max_pages]; seq_lens int32 [B].
@@ -144,8 +143,7 @@ def decode_attn_paged(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch
     if lse is None and want_lse:
         lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
     _need_cuda(out, lse)
-    d = paged_desc(q, kv_pages, page_table, k_scale=k_scale, v_scale=v_scale, workers=workers,
-                   snap_pages=snap_pages)
+    d = paged_desc(q, kv_pages, page_table, k_scale=k_scale, v_scale=v_scale, workers=workers)
     st = _lib.decode_attn_paged(ctypes.byref(d), _ptr(q), _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens),
                                 float(scale), _ptr(out), _ptr(lse), _stream(stream))
     _check(st, "decode_attn_paged")
@@ -154,7 +152,7 @@ def decode_attn_paged(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch
 
 def decode_attn_mla(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
                     scale: float, v_dim: int = 512, out: Optional[torch.Tensor] = None,
-                    lse: Optional[torch.Tensor] = None, *, workers: int = 0, snap_pages: int = 0,
+                    lse: Optional[torch.Tensor] = None, *, workers: int = 0,
                     want_lse: bool = True, stream=None):
     """Absorbed MLA decode.  q bf16 [B][H][576]; kv_pages bf16 [num_pages][P][576].
     Returns (out bf16 [B][H][v_dim], lse fp32 [B][H] or None)."""
@@ -166,28 +164,25 @@ def decode_attn_mla(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.T
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     _need_cuda(out, lse)
     num_pages, P, Dk2 = kv_pages.shape
-    d = MLADesc(B, H, Dk, v_dim, P, num_pages, page_table.shape[1], workers, snap_pages)
+    d = MLADesc(B, H, Dk, v_dim, P, num_pages, page_table.shape[1], workers)
     st = _lib.decode_attn_mla(ctypes.byref(d), _ptr(q), _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens),
                               float(scale), _ptr(out), _ptr(lse), _stream(stream))
     _check(st, "decode_attn_mla")
     return out, lse
 
 
-def decode_attn_plan(seq_lens: torch.Tensor, page_size: int, units: int, workers: int, snap_pages: int,
-                     max_pages_per_seq: int, stream=None):
-    """Run the device planner alone; returns its outputs as int32 tensors."""
+def decode_attn_plan(seq_lens: torch.Tensor, page_size: int, units: int, workers: int, stream=None):
+    """Run the split-KV planner alone; returns its outputs as int32 tensors."""
     _need_cuda(seq_lens)
     B = seq_lens.shape[0]
     dev = seq_lens.device
     z = lambda *s: torch.zeros(s, dtype=torch.int32, device=dev)
-    cp, cuts, cursors = z(B + 1), z(workers + 1), z(workers + 1, 4)
-    fw, split_list, split_count = z(B * units), z(max(workers, 1)), z(1)
-    st = _lib.decode_attn_plan(B, _ptr(seq_lens), page_size, units, workers, snap_pages, max_pages_per_seq,
-                               _ptr(cp), _ptr(cuts), _ptr(cursors), _ptr(fw), _ptr(split_list), _ptr(split_count),
-                               _stream(stream))
+    active, cuts, cursors = z(1), z(workers + 1), z(workers + 1, 4)
+    fw, count = z(B * units), z(B * units)
+    st = _lib.decode_attn_plan(B, _ptr(seq_lens), page_size, units, workers, _ptr(active), _ptr(cuts),
+                               _ptr(cursors), _ptr(fw), _ptr(count), _stream(stream))
     _check(st, "decode_attn_plan")
-    return dict(cp=cp, cuts=cuts, cursors=cursors, first_worker=fw, split_list=split_list,
-                split_count=split_count)
+    return dict(active=active, cuts=cuts, cursors=cursors, first_worker=fw, piece_count=count)
 
 
 def paged_kv_gather(kv_pages: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor, mla: bool = False,
@@ -199,11 +194,11 @@ def paged_kv_gather(kv_pages: torch.Tensor, page_table: torch.Tensor, seq_lens: 
     if mla:
         num_pages, P, Dk = kv_pages.shape
         dense = torch.zeros((B, maxp * P, Dk), dtype=kv_pages.dtype, device=kv_pages.device)
-        d = PagedDesc(B, 1, 1, Dk, P, num_pages, maxp, DA_BF16, dtype_tag(kv_pages), 0, 0, None, None)
+        d = PagedDesc(B, 1, 1, Dk, P, num_pages, maxp, DA_BF16, dtype_tag(kv_pages), 0, None, None)
     else:
         num_pages, _, Hkv, P, D = kv_pages.shape
         dense = torch.zeros((B, maxp * P, 2, Hkv, D), dtype=kv_pages.dtype, device=kv_pages.device)
-        d = PagedDesc(B, Hkv, Hkv, D, P, num_pages, maxp, DA_F32, dtype_tag(kv_pages), 0, 0, None, None)
+        d = PagedDesc(B, Hkv, Hkv, D, P, num_pages, maxp, DA_F32, dtype_tag(kv_pages), 0, None, None)
     st = _lib.paged_kv_gather(ctypes.byref(d), 1 if mla else 0, _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens),
                               _ptr(dense), _stream(stream))
     _check(st, "paged_kv_gather")

@@ -23,7 +23,7 @@ ARCH = os.environ.get("DA_OFFLOAD_ARCH", "gfx950")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
+          "-Wall", "-Wno-unused-function", "-Wno-unused-variable", "-Wno-inline-asm"]
 
 
 def hipcc() -> str:

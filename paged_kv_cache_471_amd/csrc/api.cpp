@@ -29,6 +29,11 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ---------------------------------------------------------------- workspace
 
+// One buffer per (device, stream), carved into: the plan summary (W, active
+// workers), the per-stream (first unit, pieces) records, and the partial slots
+// of split streams: 2 * workers slots of [heads][dim] fp32 values and [heads]
+// log2-sum-exps.  Nothing in it needs an initial value: every call writes what
+// it later reads.
 struct Workspace {
     void* ptr = nullptr;
     size_t bytes = 0;
@@ -67,36 +72,35 @@ int get_workspace(hipStream_t stream, size_t bytes, void** out) {
     return DA_OK;
 }
 
-// Carves the planner's and the merge's buffers out of one workspace.
-struct PlanBuffers {
-    int32_t* cp;
-    int32_t* cuts;
-    int4* cursors;
-    int32_t* first_worker;
-    int32_t* split_list;
-    int32_t* split_count;
+struct SplitBuffers {
+    int2* plan_info;
+    int2* stream_info;
     float* o_part;
     float* lse_part;
 };
 
-size_t layout(int B, int U, int G, int group, int dim, char* base, PlanBuffers* pb) {
+size_t split_layout(int streams, int G, int heads, int dim, char* base, SplitBuffers* sb) {
     size_t off = 0;
     auto take = [&](size_t bytes) -> char* {
         char* p = base ? base + off : nullptr;
         off = round_up(off + bytes, 256);
         return p;
     };
-    PlanBuffers t;
-    t.cp = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (B + 1)));
-    t.cuts = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (G + 1)));
-    t.cursors = reinterpret_cast<int4*>(take(sizeof(int4) * (G + 1)));
-    t.first_worker = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * static_cast<size_t>(B) * U));
-    t.split_list = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * G));
-    t.split_count = reinterpret_cast<int32_t*>(take(sizeof(int32_t)));
-    t.o_part = reinterpret_cast<float*>(take(sizeof(float) * 2 * static_cast<size_t>(G) * group * dim));
-    t.lse_part = reinterpret_cast<float*>(take(sizeof(float) * 2 * static_cast<size_t>(G) * group));
-    if (pb) *pb = t;
+    SplitBuffers t;
+    t.plan_info = reinterpret_cast<int2*>(take(sizeof(int2)));
+    t.stream_info = reinterpret_cast<int2*>(take(sizeof(int2) * static_cast<size_t>(streams)));
+    t.o_part = reinterpret_cast<float*>(take(sizeof(float) * 2 * static_cast<size_t>(G) * heads * dim));
+    t.lse_part = reinterpret_cast<float*>(take(sizeof(float) * 2 * static_cast<size_t>(G) * heads));
+    if (sb) *sb = t;
     return off;
+}
+
+int get_split_buffers(hipStream_t s, int streams, int G, int heads, int dim, SplitBuffers* sb) {
+    void* base = nullptr;
+    int st = get_workspace(s, split_layout(streams, G, heads, dim, nullptr, nullptr), &base);
+    if (st != DA_OK) return st;
+    split_layout(streams, G, heads, dim, static_cast<char*>(base), sb);
+    return DA_OK;
 }
 
 // ---------------------------------------------------------------- kernel timer
@@ -151,12 +155,12 @@ int device_cus(int* cus) {
     return DA_OK;
 }
 
-// ---------------------------------------------------------------- GQA validation
+// ---------------------------------------------------------------- validation
 
 int check_paged(const da_paged_desc* d) {
     if (d == nullptr) return DA_ERR_NULL;
     if (d->batch < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->head_dim < 1 || d->page_size < 1 ||
-        d->num_pages < 1 || d->max_pages_per_seq < 1 || d->workers < 0 || d->snap_pages < 0)
+        d->num_pages < 1 || d->max_pages_per_seq < 1 || d->workers < 0)
         return DA_ERR_SHAPE;
     if (d->num_q_heads % d->num_kv_heads != 0) return DA_ERR_SHAPE;
     const bool qok = d->q_dtype == DA_F32 || d->q_dtype == DA_BF16;
@@ -170,7 +174,7 @@ int check_paged(const da_paged_desc* d) {
     if (d->head_dim != 64 && d->head_dim != 128) return DA_ERR_UNSUPPORTED;
     if (d->page_size != 16) return DA_ERR_UNSUPPORTED;
     if (group != 1 && group != 2 && group != 4 && group != 8) return DA_ERR_UNSUPPORTED;
-    if (d->batch > da::kPlanMaxBatch || d->workers > da::kPlanMaxWorkers) return DA_ERR_UNSUPPORTED;
+    if (d->batch > da::kMaxBatch || d->workers > da::kMaxWorkers) return DA_ERR_UNSUPPORTED;
     const int64_t units_bound = static_cast<int64_t>(d->num_kv_heads) * d->batch * d->max_pages_per_seq;
     if (units_bound >= (int64_t(1) << 31)) return DA_ERR_UNSUPPORTED;
     if (static_cast<int64_t>(d->max_pages_per_seq) * d->page_size >= (int64_t(1) << 31)) return DA_ERR_SHAPE;
@@ -190,7 +194,37 @@ int resolve_gqa_workers(const da_paged_desc* d, int* G) {
     const int waves = da::gqa_waves_per_cu(d->q_dtype, d->kv_dtype, d->head_dim, group);
     if (waves <= 0) return DA_ERR_UNSUPPORTED;
     int g = cus * waves;
-    if (g > da::kPlanMaxWorkers) g = da::kPlanMaxWorkers;
+    if (g > da::kMaxWorkers) g = da::kMaxWorkers;
+    *G = g;
+    return DA_OK;
+}
+
+int check_mla(const da_mla_desc* d) {
+    if (d == nullptr) return DA_ERR_NULL;
+    if (d->batch < 0 || d->num_heads < 1 || d->latent_dim < 1 || d->v_dim < 1 || d->page_size < 1 ||
+        d->num_pages < 1 || d->max_pages_per_seq < 1 || d->workers < 0)
+        return DA_ERR_SHAPE;
+    if (d->v_dim > d->latent_dim) return DA_ERR_SHAPE;
+    if (d->latent_dim != da::kMlaLatent || d->v_dim != da::kMlaV) return DA_ERR_UNSUPPORTED;
+    if (d->page_size % da::kMlaChunk != 0 || d->page_size > 256) return DA_ERR_UNSUPPORTED;
+    if (!da::mla_heads_supported(d->num_heads)) return DA_ERR_UNSUPPORTED;
+    if (d->batch > da::kMaxBatch || d->workers > da::kMlaMaxWorkers) return DA_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(d->batch) * d->max_pages_per_seq >= (int64_t(1) << 31)) return DA_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(d->max_pages_per_seq) * d->page_size >= (int64_t(1) << 31)) return DA_ERR_SHAPE;
+    return DA_OK;
+}
+
+int resolve_mla_workers(const da_mla_desc* d, int* G) {
+    if (d->workers > 0) {
+        *G = d->workers;
+        return DA_OK;
+    }
+    int cus = 0;
+    int st = device_cus(&cus);
+    if (st != DA_OK) return st;
+    int g = cus * da::mla_blocks_per_cu();
+    if (g <= 0) return DA_ERR_UNSUPPORTED;
+    if (g > da::kMlaMaxWorkers) g = da::kMlaMaxWorkers;
     *G = g;
     return DA_OK;
 }
@@ -259,13 +293,11 @@ int decode_attn_paged(const da_paged_desc* d, const void* q, const void* kv_page
     if (st != DA_OK) return st;
     if (q == nullptr || kv_pages == nullptr || page_table == nullptr || seq_lens == nullptr || out == nullptr)
         return DA_ERR_NULL;
-    const int elem_q = d->q_dtype == DA_F32 ? 4 : 2;
     const int elem_kv = d->kv_dtype == DA_F32 ? 4 : (d->kv_dtype == DA_BF16 ? 2 : 1);
     const size_t lane_bytes = static_cast<size_t>(d->head_dim / 16) * elem_kv;
-    if (!aligned(kv_pages, lane_bytes < 16 ? lane_bytes : 16) || !aligned(q, 8) || !aligned(out, 8) ||
+    if (!aligned(kv_pages, lane_bytes < 16 ? lane_bytes : 16) || !aligned(q, 16) || !aligned(out, 16) ||
         !aligned(lse, 4) || !aligned(page_table, 4) || !aligned(seq_lens, 4))
         return DA_ERR_SHAPE;
-    (void)elem_q;
     if (!(scale == scale)) return DA_ERR_SHAPE;
     if (d->batch == 0) return DA_OK;
 
@@ -273,35 +305,11 @@ int decode_attn_paged(const da_paged_desc* d, const void* q, const void* kv_page
     int G = 0;
     st = resolve_gqa_workers(d, &G);
     if (st != DA_OK) return st;
-    const int U = d->num_kv_heads;
     const int group = d->num_q_heads / d->num_kv_heads;
-    const size_t bytes = layout(d->batch, U, G, group, d->head_dim, nullptr, nullptr);
-    void* ws = nullptr;
-    st = get_workspace(s, bytes, &ws);
+    const int streams = d->batch * d->num_kv_heads;
+    SplitBuffers sb;
+    st = get_split_buffers(s, streams, G, group, d->head_dim, &sb);
     if (st != DA_OK) return st;
-    PlanBuffers pb;
-    layout(d->batch, U, G, group, d->head_dim, static_cast<char*>(ws), &pb);
-
-    da::PlanArgs pa{};
-    pa.seq_lens = seq_lens;
-    pa.batch = d->batch;
-    pa.page_size = d->page_size;
-    pa.units = U;
-    pa.workers = G;
-    pa.snap = d->snap_pages;
-    pa.cp = pb.cp;
-    pa.cuts = pb.cuts;
-    pa.cursors = pb.cursors;
-    pa.first_worker = pb.first_worker;
-    pa.split_list = pb.split_list;
-    pa.split_count = pb.split_count;
-    pa.out = out;
-    pa.out_elem_bytes = elem_q;
-    pa.lse = lse;
-    pa.heads = d->num_q_heads;
-    pa.out_dim = d->head_dim;
-    hipError_t e = da::launch_plan(pa, s);
-    if (e != hipSuccess) return hip_fail(e);
 
     da::GqaArgs ga{};
     ga.q = q;
@@ -317,58 +325,99 @@ int decode_attn_paged(const da_paged_desc* d, const void* q, const void* kv_page
     ga.page_size = d->page_size;
     ga.max_pages = d->max_pages_per_seq;
     ga.workers = G;
-    ga.cuts = pb.cuts;
-    ga.cursors = pb.cursors;
+    ga.plan_info = sb.plan_info;
+    ga.stream_info = sb.stream_info;
     ga.out = out;
     ga.lse = lse;
-    ga.o_part = pb.o_part;
-    ga.lse_part = pb.lse_part;
-    e = da::launch_gqa(d->q_dtype, d->kv_dtype, d->head_dim, group, ga, s, next_kernel_events());
+    ga.o_part = sb.o_part;
+    ga.lse_part = sb.lse_part;
+    hipError_t e = da::launch_gqa(d->q_dtype, d->kv_dtype, d->head_dim, group, ga, s, next_kernel_events());
     if (e != hipSuccess) return hip_fail(e);
 
     da::MergeArgs ma{};
     ma.seq_lens = seq_lens;
-    ma.batch = d->batch;
-    ma.page_size = d->page_size;
-    ma.units = U;
-    ma.workers = G;
+    ma.plan_info = sb.plan_info;
+    ma.stream_info = sb.stream_info;
+    ma.o_part = sb.o_part;
+    ma.lse_part = sb.lse_part;
+    ma.out = out;
+    ma.lse = lse;
+    ma.units = d->num_kv_heads;
     ma.group = group;
     ma.dim = d->head_dim;
-    ma.q_heads = d->num_q_heads;
-    ma.cp = pb.cp;
-    ma.cuts = pb.cuts;
-    ma.first_worker = pb.first_worker;
-    ma.split_list = pb.split_list;
-    ma.split_count = pb.split_count;
-    ma.o_part = pb.o_part;
-    ma.lse_part = pb.lse_part;
-    ma.out = out;
+    ma.heads_per_block = 1;
     ma.out_is_bf16 = d->q_dtype == DA_BF16;
-    ma.lse = lse;
-    int grid = G * group;
-    if (grid > 2048) grid = 2048;
-    e = da::launch_merge(ma, grid, s);
+    e = da::launch_merge(ma, streams, s);
     if (e != hipSuccess) return hip_fail(e);
     return DA_OK;
 }
 
 int decode_attn_mla(const da_mla_desc* d, const void* q, const void* kv_pages, const int32_t* page_table,
                     const int32_t* seq_lens, float scale, void* out, float* lse, void* stream) {
-    (void)d; (void)q; (void)kv_pages; (void)page_table; (void)seq_lens; (void)scale; (void)out; (void)lse;
-    (void)stream;
-    return DA_ERR_UNSUPPORTED;
+    int st = check_mla(d);
+    if (st != DA_OK) return st;
+    if (q == nullptr || kv_pages == nullptr || page_table == nullptr || seq_lens == nullptr || out == nullptr)
+        return DA_ERR_NULL;
+    if (!aligned(kv_pages, 16) || !aligned(q, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
+        !aligned(page_table, 4) || !aligned(seq_lens, 4))
+        return DA_ERR_SHAPE;
+    if (!(scale == scale)) return DA_ERR_SHAPE;
+    if (d->batch == 0) return DA_OK;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int G = 0;
+    st = resolve_mla_workers(d, &G);
+    if (st != DA_OK) return st;
+    SplitBuffers sb;
+    st = get_split_buffers(s, d->batch, G, d->num_heads, d->v_dim, &sb);
+    if (st != DA_OK) return st;
+
+    da::MlaArgs ma{};
+    ma.q = q;
+    ma.kv = kv_pages;
+    ma.page_table = page_table;
+    ma.seq_lens = seq_lens;
+    ma.scale_log2 = scale * 1.4426950408889634f;
+    ma.batch = d->batch;
+    ma.heads = d->num_heads;
+    ma.page_size = d->page_size;
+    ma.max_pages = d->max_pages_per_seq;
+    ma.workers = G;
+    ma.plan_info = sb.plan_info;
+    ma.stream_info = sb.stream_info;
+    ma.out = out;
+    ma.lse = lse;
+    ma.o_part = sb.o_part;
+    ma.lse_part = sb.lse_part;
+    hipError_t e = da::launch_mla(ma, s, next_kernel_events());
+    if (e != hipSuccess) return hip_fail(e);
+
+    da::MergeArgs mg{};
+    mg.seq_lens = seq_lens;
+    mg.plan_info = sb.plan_info;
+    mg.stream_info = sb.stream_info;
+    mg.o_part = sb.o_part;
+    mg.lse_part = sb.lse_part;
+    mg.out = out;
+    mg.lse = lse;
+    mg.units = 1;
+    mg.group = d->num_heads;
+    mg.dim = d->v_dim;
+    mg.heads_per_block = d->num_heads >= 8 ? 8 : d->num_heads;
+    mg.out_is_bf16 = 1;
+    e = da::launch_merge(mg, d->batch, s);
+    if (e != hipSuccess) return hip_fail(e);
+    return DA_OK;
 }
 
 int decode_attn_plan(int32_t batch, const int32_t* seq_lens, int32_t page_size, int32_t units, int32_t workers,
-                     int32_t snap_pages, int32_t max_pages_per_seq, int32_t* cp, int32_t* cuts, int32_t* cursors,
-                     int32_t* first_worker, int32_t* split_list, int32_t* split_count, void* stream) {
-    if (seq_lens == nullptr || cp == nullptr || cuts == nullptr || cursors == nullptr || first_worker == nullptr ||
-        split_list == nullptr || split_count == nullptr)
+                     int32_t* active, int32_t* cuts, int32_t* cursors, int32_t* first_worker, int32_t* piece_count,
+                     void* stream) {
+    if (seq_lens == nullptr || active == nullptr || cuts == nullptr || cursors == nullptr ||
+        first_worker == nullptr || piece_count == nullptr)
         return DA_ERR_NULL;
-    if (batch < 1 || page_size < 1 || units < 1 || workers < 1 || snap_pages < 0 || max_pages_per_seq < 1)
-        return DA_ERR_SHAPE;
-    if (batch > da::kPlanMaxBatch || workers > da::kPlanMaxWorkers) return DA_ERR_UNSUPPORTED;
-    if (static_cast<int64_t>(units) * batch * max_pages_per_seq >= (int64_t(1) << 31)) return DA_ERR_UNSUPPORTED;
+    if (batch < 1 || page_size < 1 || units < 1 || workers < 1) return DA_ERR_SHAPE;
+    if (batch > da::kMaxBatch || workers > da::kMaxWorkers) return DA_ERR_UNSUPPORTED;
     if (!aligned(cursors, 16)) return DA_ERR_SHAPE;
     da::PlanArgs pa{};
     pa.seq_lens = seq_lens;
@@ -376,16 +425,12 @@ int decode_attn_plan(int32_t batch, const int32_t* seq_lens, int32_t page_size, 
     pa.page_size = page_size;
     pa.units = units;
     pa.workers = workers;
-    pa.snap = snap_pages;
-    pa.cp = cp;
+    pa.active = active;
     pa.cuts = cuts;
     pa.cursors = reinterpret_cast<int4*>(cursors);
     pa.first_worker = first_worker;
-    pa.split_list = split_list;
-    pa.split_count = split_count;
-    pa.out = nullptr;
-    pa.lse = nullptr;
-    hipError_t e = da::launch_plan(pa, static_cast<hipStream_t>(stream));
+    pa.piece_count = piece_count;
+    hipError_t e = da::launch_plan_debug(pa, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e);
     return DA_OK;
 }
@@ -422,18 +467,24 @@ int paged_kv_gather(const da_paged_desc* d, int32_t mla, const void* kv_pages, c
 
 int decode_attn_default_workers(const da_paged_desc* gqa, const da_mla_desc* mla, int32_t* workers) {
     if (workers == nullptr || (gqa == nullptr) == (mla == nullptr)) return DA_ERR_NULL;
+    int G = 0;
+    int st = DA_OK;
     if (gqa != nullptr) {
-        int st = check_paged(gqa);
+        st = check_paged(gqa);
         if (st != DA_OK) return st;
-        int G = 0;
         da_paged_desc dd = *gqa;
         dd.workers = 0;
         st = resolve_gqa_workers(&dd, &G);
+    } else {
+        st = check_mla(mla);
         if (st != DA_OK) return st;
-        *workers = G;
-        return DA_OK;
+        da_mla_desc dd = *mla;
+        dd.workers = 0;
+        st = resolve_mla_workers(&dd, &G);
     }
-    return DA_ERR_UNSUPPORTED;
+    if (st != DA_OK) return st;
+    *workers = G;
+    return DA_OK;
 }
 
 }  // extern "C"

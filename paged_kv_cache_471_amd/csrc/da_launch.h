@@ -6,26 +6,20 @@
 
 namespace da {
 
-// Bounds of the single-workgroup planner: its LDS holds cp [batch + 1], the
-// cuts [workers + 1] and a 1024-entry scan buffer within 64 KiB.
-constexpr int kPlanMaxBatch = 8192;
-constexpr int kPlanMaxWorkers = 6144;
+// Largest batch the wave planner accepts: each lane scans ceil(B / 64) requests.
+constexpr int kMaxBatch = 8192;
+// Largest number of workers (waves for GQA, workgroups for MLA) per launch.
+constexpr int kMaxWorkers = 16384;
 
+// Debug run of the wave planner: worker g writes what its share would be.
 struct PlanArgs {
     const int32_t* seq_lens;
-    int batch, page_size, units, workers, snap;
-    int32_t* cp;            // [batch + 1]
-    int32_t* cuts;          // [workers + 1]
-    int4* cursors;          // [workers + 1]
+    int batch, page_size, units, workers;
+    int32_t* active;        // [1]
+    int32_t* cuts;          // [workers + 1]; W for g >= active
+    int4* cursors;          // [workers + 1]; (batch, 0, 0, 0) at W
     int32_t* first_worker;  // [batch * units]
-    int32_t* split_list;    // [workers]
-    int32_t* split_count;   // [1]
-    // outputs of empty requests (L == 0) are written here: out = 0, lse = -inf
-    void* out;              // may be null (planner-only runs)
-    int out_elem_bytes;
-    float* lse;             // may be null
-    int heads;              // query heads per request
-    int out_dim;            // values per head
+    int32_t* piece_count;   // [batch * units]
 };
 
 struct GqaArgs {
@@ -37,30 +31,56 @@ struct GqaArgs {
     const float* v_scale;
     float scale_log2;       // softmax scale * log2(e)
     int batch, q_heads, kv_heads, page_size, max_pages, workers;
-    const int32_t* cuts;
-    const int4* cursors;
+    int2* plan_info;        // [1]: (W, active workers), written by worker 0
+    int2* stream_info;      // [batch * kv_heads]: (first unit, pieces) of each non-empty stream
     void* out;
     float* lse;
     float* o_part;          // [2 * workers][group][head_dim]
     float* lse_part;        // [2 * workers][group]   (log2 domain)
 };
 
+// Absorbed MLA: one head-shared latent of kMlaLatent bf16 values per token;
+// values are its first kMlaV entries.  Tokens are processed in chunks of
+// kMlaChunk (pages are a multiple of it).
+constexpr int kMlaLatent = 576;
+constexpr int kMlaV = 512;
+constexpr int kMlaChunk = 32;
+constexpr int kMlaMaxHeads = 128;
+// Each MLA worker may leave two partial slots of [heads][512] fp32 (256 KiB at
+// 128 heads); this bounds the workspace at 1 GiB.
+constexpr int kMlaMaxWorkers = 2048;
+
+struct MlaArgs {
+    const void* q;          // bf16 [batch][heads][576]
+    const void* kv;         // bf16 [num_pages][page_size][576]
+    const int32_t* page_table;
+    const int32_t* seq_lens;
+    float scale_log2;       // softmax scale * log2(e)
+    int batch, heads, page_size, max_pages, workers;
+    int2* plan_info;        // [1]: (W, active workers), written by worker 0
+    int2* stream_info;      // [batch]: (first unit, pieces) of each non-empty request
+    void* out;              // bf16 [batch][heads][512]
+    float* lse;             // fp32 [batch][heads] or null
+    float* o_part;          // [2 * workers][heads][512]
+    float* lse_part;        // [2 * workers][heads]   (log2 domain)
+};
+
+// Log-sum-exp merge of the partial slots of split streams.  One workgroup per
+// (stream, group of heads_per_block heads); streams that are empty or were not
+// split return at once.
 struct MergeArgs {
     const int32_t* seq_lens;
-    int batch, page_size, units, workers;
+    const int2* plan_info;
+    const int2* stream_info;
+    const float* o_part;    // [2 * workers][group][dim]
+    const float* lse_part;  // [2 * workers][group]  (log2 domain)
+    void* out;              // [batch][units * group][dim], bf16 or fp32
+    float* lse;             // [batch][units * group] or null
+    int units;              // streams per request (KV heads, or 1 for MLA)
     int group;              // heads per stream
     int dim;                // values per head
-    int q_heads;            // heads per request in out/lse
-    const int32_t* cp;
-    const int32_t* cuts;
-    const int32_t* first_worker;
-    const int32_t* split_list;
-    const int32_t* split_count;
-    const float* o_part;
-    const float* lse_part;
-    void* out;
+    int heads_per_block;    // divides group
     int out_is_bf16;
-    float* lse;
 };
 
 struct GatherArgs {
@@ -78,9 +98,15 @@ struct KernelEvents {
     hipEvent_t stop = nullptr;
 };
 
-hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
-hipError_t launch_merge(const MergeArgs& a, int grid, hipStream_t s);
+hipError_t launch_plan_debug(const PlanArgs& a, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, int streams, hipStream_t s);
+
+hipError_t launch_mla(const MlaArgs& a, hipStream_t s, const KernelEvents& ev);
+// Workgroups of the MLA kernel that fit on one CU at once.
+int mla_blocks_per_cu();
+// Head counts with an MLA kernel (16, 32, 64, 128).
+bool mla_heads_supported(int heads);
 
 // Returns hipErrorInvalidValue if no kernel exists for this combination.
 hipError_t launch_gqa(int q_dtype, int kv_dtype, int head_dim, int group, const GqaArgs& a, hipStream_t s,

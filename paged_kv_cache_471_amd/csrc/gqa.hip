@@ -29,11 +29,13 @@
 //    (exact products, fp32 sum), fp8 K is converted exactly to bf16 first.
 //  * At the end of a piece the four rows are merged; a piece that is the whole
 //    stream writes out/lse, otherwise (o, log2-sum-exp) goes to a partial slot
-//    that the merge kernel combines.
+//    that the merge kernel (merge.hip) combines.
+//  * Each wave plans its own share (da_plan.h): no planner launch precedes it.
 #include <hip/hip_ext.h>
 
 #include "da_common.h"
 #include "da_launch.h"
+#include "da_plan.h"
 
 namespace da {
 namespace {
@@ -109,19 +111,36 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
     const int col = lane & 15;            // dim slice
     const int g = uniform(blockIdx.x * (kGqaBlock / 64) + (threadIdx.x >> 6));
     if (g >= a.workers) return;
-    const int c0 = a.cuts[g];
-    const int n = a.cuts[g + 1] - c0;
-    if (n <= 0) return;
-
     const int Hkv = a.kv_heads;
     const int Hq = a.q_heads;
+
+    const WaveShare sh = plan_share(a.seq_lens, a.batch, kPage, Hkv, a.workers, g);
+    if (sh.has_empty) {
+        // requests with no history: out = 0, lse = -inf
+        for_each_empty_request(a.seq_lens, a.batch, a.workers, g, [&](int b) {
+            const int row_elems = Hq * D;
+            if constexpr (QT == kF32) {
+                float* o = static_cast<float*>(a.out) + static_cast<int64_t>(b) * row_elems;
+                for (int i = lane; i < row_elems; i += 64) o[i] = 0.0f;
+            } else {
+                uint16_t* o = static_cast<uint16_t*>(a.out) + static_cast<int64_t>(b) * row_elems;
+                for (int i = lane; i < row_elems; i += 64) o[i] = 0;
+            }
+            if (a.lse != nullptr)
+                for (int h = lane; h < Hq; h += 64) a.lse[static_cast<int64_t>(b) * Hq + h] = -__builtin_inff();
+        });
+    }
+    const int NA = sh.active;             // active workers
+    if (g == 0 && lane == 0) *a.plan_info = make_int2(static_cast<int>(sh.W), NA);
+    if (g >= NA) return;
+    const int64_t c0 = sh.c0;
+    const int n = static_cast<int>(sh.c1 - sh.c0);
     const char* kvb = static_cast<const char*>(a.kv);
     const int64_t block_elems = static_cast<int64_t>(kPage) * D;   // one (page, K|V, head) block
     const int lane_off = (row * D + col * DL) * EB;                  // bytes within a 4-row group
 
-    const int4 start = a.cursors[g];
     Cursor cc;                                 // compute cursor
-    cc.b = start.x; cc.j = start.y; cc.p = start.z;
+    cc.b = sh.b; cc.j = sh.j; cc.p = sh.p;
     cc.len = a.seq_lens[cc.b];
     cc.pages = (cc.len + kPage - 1) / kPage;
     Cursor lc = cc;                            // load cursor (one unit ahead)
@@ -349,12 +368,23 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
         pid = page_id(lc);
     }
 
+    // The wave holding a stream's first piece records where the stream starts
+    // and over how many workers it is split, for the merge kernel.
+    auto record_stream = [&](int64_t start) {
+        if (lane != 0) return;
+        const int gf = first_worker_of(start, sh.W, NA);
+        const int gl = last_worker_of(start + cc.pages, sh.W, NA);
+        a.stream_info[cc.b * Hkv + cc.j] = make_int2(static_cast<int>(start), gl - gf + 1);
+    };
+
     // after computing unit k: close the piece if the stream or the share ends
     auto end_of_unit = [&](int k) {
         const bool stream_end = (cc.p == cc.pages - 1);
         const bool share_end = (k == n - 1);
         if (stream_end || share_end) {
-            finalize(stream_end && piece_p0 == 0, first_piece ? g : a.workers + g);
+            const bool whole = stream_end && piece_p0 == 0;
+            finalize(whole, first_piece ? g : NA + g);
+            if (piece_p0 == 0) record_stream(c0 + k - cc.p);
             if (!share_end) {
                 cursor_next(cc, a.seq_lens, Hkv);
                 first_piece = false;

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def _desc(lib, **kw):
     base = dict(batch=4, num_q_heads=8, num_kv_heads=2, head_dim=64, page_size=16, num_pages=10,
-                max_pages_per_seq=4, q_dtype=0, kv_dtype=0, workers=0, snap_pages=0, k_scale=None, v_scale=None)
+                max_pages_per_seq=4, q_dtype=0, kv_dtype=0, workers=0, k_scale=None, v_scale=None)
     base.update(kw)
     return lib.PagedDesc(**base)
 
@@ -71,8 +71,10 @@ def test_null_pointers_rejected(lib):
     assert L.decode_attn_paged(None, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, None) == -1
     assert L.decode_attn_paged(ctypes.byref(d), None, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, None) == -1
     assert L.decode_attn_paged(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0.1, None, FAKE, None) == -1
-    assert L.decode_attn_plan(4, None, 16, 1, 8, 0, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
-    assert L.decode_attn_plan(4, FAKE, 16, 1, 0, 0, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2
+    assert L.decode_attn_plan(4, None, 16, 1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert L.decode_attn_plan(4, FAKE, 16, 1, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2
+    assert L.decode_attn_plan(9000, FAKE, 16, 1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -4
+    assert L.decode_attn_mla(None, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, None) == -1
     assert L.paged_kv_gather(None, 0, FAKE, FAKE, FAKE, FAKE, None) == -1
 
 
@@ -86,3 +88,33 @@ def test_status_strings(lib):
     L = lib.lib()
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert L.decode_attn_status_str(s)
+
+
+def _mla_desc(lib, **kw):
+    base = dict(batch=4, num_heads=128, latent_dim=576, v_dim=512, page_size=64, num_pages=10,
+                max_pages_per_seq=4, workers=0)
+    base.update(kw)
+    return lib.MLADesc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_heads=48), -4),                         # no kernel for 48 heads
+    (dict(num_heads=256), -4),
+    (dict(latent_dim=512, v_dim=512), -4),            # only the 576 / 512 latent
+    (dict(v_dim=600), -2),                            # values wider than the latent
+    (dict(page_size=16), -4),                         # pages must hold whole 32-token chunks
+    (dict(page_size=48), -4),
+    (dict(workers=4096), -4),
+    (dict(batch=-2), -2),
+    (dict(num_pages=0), -2),
+])
+def test_invalid_mla_descriptors_rejected(lib, kw, status):
+    d = _mla_desc(lib, **kw)
+    st = lib.lib().decode_attn_mla(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0.05, FAKE, FAKE, None)
+    assert st == status, lib.lib().decode_attn_status_str(st)
+
+
+def test_mla_misaligned_rejected(lib):
+    d = _mla_desc(lib)
+    st = lib.lib().decode_attn_mla(ctypes.byref(d), FAKE + 8, FAKE, FAKE, FAKE, 0.05, FAKE, FAKE, None)
+    assert st == -2
