@@ -69,6 +69,17 @@ def workload_desc(cfg) -> str:
             f"lengths {cfg.lengths}")
 
 
+def config_fields(cfg, runner):
+    import workloads as wl
+    d = {"workload": workload_desc(cfg), "batch": runner.batch, "q_heads": cfg.q_heads}
+    if isinstance(cfg, wl.MLAConfig):
+        d.update(latent_dim=cfg.latent_dim, v_dim=cfg.v_dim)
+    else:
+        d.update(kv_heads=cfg.kv_heads, head_dim=cfg.head_dim)
+    d.update(page_size=cfg.page_size, sum_seq_len=runner.tokens, seed=cfg.seed)
+    return d
+
+
 class GqaRunner:
     def __init__(self, cfg, sets=2):
         import torch
@@ -288,18 +299,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.DTYPE_NAMES[cfg.kv_dtype],
+        "dtype": "bf16" if isinstance(cfg, wl.MLAConfig) else wl.DTYPE_NAMES[cfg.kv_dtype],
         "data": "synthetic",
-        "config": {"workload": workload_desc(cfg), "batch": runner.batch, "q_heads": cfg.q_heads,
-                   "kv_heads": cfg.kv_heads, "head_dim": cfg.head_dim, "page_size": cfg.page_size,
-                   "sum_seq_len": runner.tokens, "seed": cfg.seed},
+        "config": config_fields(cfg, runner),
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": runner.batch / (ms * 1e-3),
         "kv_tokens_per_s": runner.tokens / (ms * 1e-3),
         "algorithmic_bytes_per_step": runner.bytes,
         "roofline": {
             "bound": "hbm",
-            "kernel": "gqa_attn_kernel",
+            "kernel": "mla_attn_kernel" if isinstance(cfg, wl.MLAConfig) else "gqa_attn_kernel",
             "achieved": round(kern_gbs, 2) if kern_gbs else None,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -222,7 +222,7 @@ int resolve_mla_workers(const da_mla_desc* d, int* G) {
     int cus = 0;
     int st = device_cus(&cus);
     if (st != DA_OK) return st;
-    int g = cus * da::mla_blocks_per_cu();
+    int g = cus * da::mla_blocks_per_cu() / da::mla_blocks_per_worker(d->num_heads);
     if (g <= 0) return DA_ERR_UNSUPPORTED;
     if (g > da::kMlaMaxWorkers) g = da::kMlaMaxWorkers;
     *G = g;

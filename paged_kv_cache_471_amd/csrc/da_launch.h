@@ -107,6 +107,8 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t s, const KernelEvents& ev);
 int mla_blocks_per_cu();
 // Head counts with an MLA kernel (16, 32, 64, 128).
 bool mla_heads_supported(int heads);
+// Workgroups that share one MLA worker's share (one per 64-head group).
+int mla_blocks_per_worker(int heads);
 
 // Returns hipErrorInvalidValue if no kernel exists for this combination.
 hipError_t launch_gqa(int q_dtype, int kv_dtype, int head_dim, int group, const GqaArgs& a, hipStream_t s,
