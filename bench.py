@@ -33,7 +33,7 @@ METRIC = "decode-attention KV GB/s (% of HBM peak) + tokens/s per step, 1 MI355X
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK = 2.5e15         # dense bf16 FLOP/s, MI355X
 KERNEL_SOURCES = ["paged_kv_cache_471_amd/csrc/gqa.hip", "paged_kv_cache_471_amd/csrc/da_common.h",
-                  "paged_kv_cache_471_amd/csrc/da_launch.h"]
+                  "paged_kv_cache_471_amd/csrc/da_launch.h", "paged_kv_cache_471_amd/csrc/da_plan.h"]
 PMC_FILE = os.path.join(ROOT, "profiles", "gqa_llama8b_pmc.md")
 
 
