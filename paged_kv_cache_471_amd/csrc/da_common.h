@@ -73,6 +73,15 @@ __device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Wave-uniform 32-bit read through the scalar data cache (a read; the value is
+// ready when the call returns).  Used for page ids and lengths, so that they
+// do not queue behind the vector loads of the KV stream.
+__device__ __forceinline__ int sload_i32(const int32_t* p) {
+    int v;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+    return v;
+}
+
 // Address function of the paged GQA cache [num_pages][2][Hkv][P][D]:
 // element offset of (page, sel = 0 key / 1 value, kv head, slot, dim 0).
 __device__ __forceinline__ int64_t gqa_kv_offset(int page, int sel, int head, int slot, int num_kv_heads,

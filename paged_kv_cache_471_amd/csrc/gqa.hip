@@ -50,6 +50,9 @@ struct Cfg {
     static constexpr int NW = DL * EB / 4;        // 32-bit words per lane per token row
     static constexpr bool kDot = (KV != kF32);    // bf16 pairs + dot2 for q.k
     static constexpr int QW = kDot ? DL / 2 : DL; // q registers per head
+    // page buffers (NB - 1 pages in flight): as deep as registers allow at
+    // two waves per SIMD
+    static constexpr int NB = (GS >= 8 ? 2 : (NW <= 2 ? 4 : (NW == 4 && GS <= 4 ? 3 : 2)));
     static_assert(NW >= 1, "lane slice must be at least one word");
 };
 
@@ -96,7 +99,7 @@ __device__ __forceinline__ void cursor_next(Cursor& c, const int32_t* seq_lens, 
     c.j = 0;
     do {
         ++c.b;
-        c.len = seq_lens[c.b];
+        c.len = sload_i32(seq_lens + c.b);
         c.pages = (c.len + kPage - 1) / kPage;
     } while (c.pages == 0);
 }
@@ -141,12 +144,12 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
 
     Cursor cc;                                 // compute cursor
     cc.b = sh.b; cc.j = sh.j; cc.p = sh.p;
-    cc.len = a.seq_lens[cc.b];
+    cc.len = sload_i32(a.seq_lens + cc.b);
     cc.pages = (cc.len + kPage - 1) / kPage;
     Cursor lc = cc;                            // load cursor (one unit ahead)
 
     auto page_id = [&](const Cursor& c) -> int {
-        return a.page_table[static_cast<int64_t>(c.b) * a.max_pages + c.p];
+        return sload_i32(a.page_table + static_cast<int64_t>(c.b) * a.max_pages + c.p);
     };
     auto issue = [&](PageBuf<NW>& buf, int pid, int j) {
         const char* kbase = kvb + (gqa_kv_offset(pid, 0, j, 0, Hkv, kPage, D)) * EB + lane_off;
@@ -360,12 +363,19 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
     bool first_piece = true;
     int piece_p0 = cc.p;
 
-    PageBuf<NW> A, Bf;
+    // NB page buffers: NB - 1 pages of K and V in flight ahead of the one computed
+    constexpr int NB = C::NB;
+    PageBuf<NW> buf[NB];
     int pid = page_id(lc);
-    issue(A, pid, lc.j);
-    if (n > 1) {
-        cursor_next(lc, a.seq_lens, Hkv);
-        pid = page_id(lc);
+#pragma unroll
+    for (int u = 0; u < NB - 1; ++u) {
+        if (u < n) {
+            issue(buf[u], pid, lc.j);
+            if (u + 1 < n) {
+                cursor_next(lc, a.seq_lens, Hkv);
+                pid = page_id(lc);
+            }
+        }
     }
 
     // The wave holding a stream's first piece records where the stream starts
@@ -399,26 +409,19 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
     };
 
     for (int k = 0; k < n;) {
-        if (k + 1 < n) {
-            issue(Bf, pid, lc.j);
-            if (k + 2 < n) {
-                cursor_next(lc, a.seq_lens, Hkv);
-                pid = page_id(lc);
+#pragma unroll
+        for (int r = 0; r < NB; ++r) {          // unit k sits in buf[r] (k % NB == r)
+            if (k + NB - 1 < n) {
+                issue(buf[(r + NB - 1) % NB], pid, lc.j);
+                if (k + NB < n) {
+                    cursor_next(lc, a.seq_lens, Hkv);
+                    pid = page_id(lc);
+                }
             }
+            process(buf[r]);
+            end_of_unit(k);
+            if (++k >= n) break;
         }
-        process(A);
-        end_of_unit(k);
-        if (++k >= n) break;
-        if (k + 1 < n) {
-            issue(A, pid, lc.j);
-            if (k + 2 < n) {
-                cursor_next(lc, a.seq_lens, Hkv);
-                pid = page_id(lc);
-            }
-        }
-        process(Bf);
-        end_of_unit(k);
-        ++k;
     }
 }
 

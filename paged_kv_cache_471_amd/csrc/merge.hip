@@ -21,32 +21,9 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int x = 32; x >= 1; x >>= 1) v = fmaxf(v, __shfl_xor(v, x, 64));
-    return v;
-}
-
-// Reduce v over aligned segments of `seg` consecutive threads (seg a power of
-// two, 1..256) with op; every thread of a segment gets the segment's result.
-template <bool MAX>
-__device__ __forceinline__ float segment_reduce(float v, int seg, float* red) {
-    const int t = threadIdx.x;
-    red[t] = v;
-    __syncthreads();
-    for (int off = seg >> 1; off >= 1; off >>= 1) {
-        if ((t & (seg - 1)) < off) red[t] = MAX ? fmaxf(red[t], red[t + off]) : red[t] + red[t + off];
-        __syncthreads();
-    }
-    const float r = red[t & ~(seg - 1)];
-    __syncthreads();
-    return r;
-}
-
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
-    __shared__ float red[kThreads];
     __shared__ float4 part[kThreads];
-    __shared__ float sM[8], sZ[8];
+    __shared__ float pm[kThreads], pz[kThreads];
     const int t = threadIdx.x;
     const int nh = a.heads_per_block;
     const int per_stream = a.group / nh;
@@ -54,11 +31,12 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     const int h0 = (blockIdx.x % per_stream) * nh;
     const int b = s / a.units;
     const int j = s % a.units;
-    if (a.seq_lens[b] == 0) return;
+    // independent loads first: length, stream record, plan summary
+    const int L = a.seq_lens[b];
     const int2 info = a.stream_info[s];
-    const int n = info.y;
-    if (n <= 1) return;
     const int2 pi = *a.plan_info;
+    if (L == 0 || info.y <= 1) return;
+    const int n = info.y;
     const int64_t W = pi.x;
     const int A = pi.y;
     const int64_t start = info.x;
@@ -66,69 +44,68 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     const int D = a.dim;
     const int G = a.group;
 
-    // per-head maximum and sum of the pieces' log2-sum-exps
-    const int tph = kThreads / nh;              // threads per head
-    const int hh = t / tph, pl = t % tph;
-    float m = -__builtin_inff();
-    for (int i = pl; i < n; i += tph)
-        m = fmaxf(m, a.lse_part[static_cast<int64_t>(slot_of(gf + i, start, W, A)) * G + h0 + hh]);
-    m = segment_reduce<true>(m, tph, red);
-    float z = 0.0f;
-    for (int i = pl; i < n; i += tph)
-        z += __builtin_amdgcn_exp2f(a.lse_part[static_cast<int64_t>(slot_of(gf + i, start, W, A)) * G + h0 + hh] - m);
-    z = segment_reduce<false>(z, tph, red);
-    if (pl == 0) {
-        sM[hh] = m;
-        sZ[hh] = z;
-        if (a.lse != nullptr)
-            a.lse[static_cast<int64_t>(b) * a.units * G + j * G + h0 + hh] = (m + __builtin_log2f(z)) * kLn2;
-    }
-    __syncthreads();
-
-    // weighted sum of the pieces' outputs, float4 columns of [nh][D]
+    // Thread (q, c): float4 column c of [nh][D], pieces i = q, q + PL, ...  Each
+    // thread folds its pieces with a running maximum, then the PL piece lanes
+    // of a column are folded in a fixed order; one round trip to memory.
     const int C4 = nh * D / 4;
-    const int PL = C4 >= kThreads ? 1 : kThreads / C4;    // piece lanes per column
-    const int q = t / (kThreads / PL) ;                   // this thread's piece lane
-    const int64_t out_base = (static_cast<int64_t>(b) * a.units * G + j * G + h0) * D;
-    for (int c0 = 0; c0 < C4; c0 += kThreads / PL) {
-        const int c = c0 + t % (kThreads / PL);
+    const int cols = C4 < kThreads ? C4 : kThreads;       // columns handled at once
+    const int PL = kThreads / cols;                       // piece lanes per column
+    const int q = t / cols;
+    const int64_t out_row = static_cast<int64_t>(b) * a.units * G + j * G + h0;
+    for (int c0 = 0; c0 < C4; c0 += cols) {
+        const int c = c0 + t % cols;
         const int h = (4 * c) / D;
-        const float M = sM[h];
+        float m = -__builtin_inff(), z = 0.0f;
         float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll 4
         for (int i = q; i < n; i += PL) {
             const int64_t sl = slot_of(gf + i, start, W, A);
-            const float w = __builtin_amdgcn_exp2f(a.lse_part[sl * G + h0 + h] - M);
+            const float l = a.lse_part[sl * G + h0 + h];
             const float4 o = reinterpret_cast<const float4*>(a.o_part + (sl * G + h0) * D)[c];
-            acc.x = __builtin_fmaf(w, o.x, acc.x);
-            acc.y = __builtin_fmaf(w, o.y, acc.y);
-            acc.z = __builtin_fmaf(w, o.z, acc.z);
-            acc.w = __builtin_fmaf(w, o.w, acc.w);
+            const float mn = fmaxf(m, l);
+            const float fo = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first piece
+            const float fn = __builtin_amdgcn_exp2f(l - mn);
+            z = z * fo + fn;
+            acc.x = acc.x * fo + fn * o.x;
+            acc.y = acc.y * fo + fn * o.y;
+            acc.z = acc.z * fo + fn * o.z;
+            acc.w = acc.w * fo + fn * o.w;
+            m = mn;
         }
         if (PL > 1) {
             part[t] = acc;
+            pm[t] = m;
+            pz[t] = z;
             __syncthreads();
             if (q == 0) {
                 for (int r = 1; r < PL; ++r) {
-                    const float4 o = part[t + r * (kThreads / PL)];
-                    acc.x += o.x;
-                    acc.y += o.y;
-                    acc.z += o.z;
-                    acc.w += o.w;
+                    const int u = t + r * cols;
+                    const float mo = pm[u];
+                    const float mn = fmaxf(m, mo);
+                    const float fs = __builtin_amdgcn_exp2f(m - mn);
+                    const float fo = __builtin_amdgcn_exp2f(mo - mn);
+                    const float4 o = part[u];
+                    z = z * fs + pz[u] * fo;
+                    acc.x = acc.x * fs + o.x * fo;
+                    acc.y = acc.y * fs + o.y * fo;
+                    acc.z = acc.z * fs + o.z * fo;
+                    acc.w = acc.w * fs + o.w * fo;
+                    m = mn;
                 }
             }
             __syncthreads();
         }
         if (q == 0) {
-            const float inv = 1.0f / sZ[h];
+            const float inv = 1.0f / z;
             if (a.out_is_bf16) {
                 const uint32_t lo = f32_to_bf16_bits(acc.x * inv) | (static_cast<uint32_t>(f32_to_bf16_bits(acc.y * inv)) << 16);
                 const uint32_t hi = f32_to_bf16_bits(acc.z * inv) | (static_cast<uint32_t>(f32_to_bf16_bits(acc.w * inv)) << 16);
-                reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + out_base)[c] = make_uint2(lo, hi);
+                reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + out_row * D)[c] = make_uint2(lo, hi);
             } else {
-                reinterpret_cast<float4*>(static_cast<float*>(a.out) + out_base)[c] =
+                reinterpret_cast<float4*>(static_cast<float*>(a.out) + out_row * D)[c] =
                     make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
             }
+            if (a.lse != nullptr && (4 * c) % D == 0) a.lse[out_row + h] = (m + __builtin_log2f(z)) * kLn2;
         }
     }
 }

@@ -80,15 +80,6 @@ struct __align__(16) Smem {
     int flags[kWaves];
 };
 
-// Wave-uniform 32-bit read through the scalar data cache (a read; the value is
-// ready when the call returns).  Used for page ids and lengths, so that they
-// do not queue behind the vector loads of the chunk ring.
-__device__ __forceinline__ int sload_i32(const int32_t* p) {
-    int v;
-    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
-    return v;
-}
-
 // Compute/load cursor over the chunks of a worker's share.  Wave-uniform.
 struct Cursor {
     int b, p, ci;      // request, page, chunk within the page
