@@ -73,6 +73,10 @@ __device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Read-only kernel data (page tables, lengths) seen through the constant
+// address space; wave-uniform reads of it compile to scalar loads.
+typedef const __attribute__((address_space(4))) int32_t cint32_t;
+
 // Wave-uniform 32-bit read through the scalar data cache (a read; the value is
 // ready when the call returns).  Used for page ids and lengths, so that they
 // do not queue behind the vector loads of the KV stream.

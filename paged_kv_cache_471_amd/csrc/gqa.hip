@@ -148,8 +148,12 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
     cc.pages = (cc.len + kPage - 1) / kPage;
     Cursor lc = cc;                            // load cursor (one unit ahead)
 
+    // Page ids are read through the constant address space: a wave-uniform
+    // read there becomes a scalar load whose wait the compiler places at the
+    // first use, one unit later, so its latency hides behind a page of work.
+    const cint32_t* page_table = (const cint32_t*)a.page_table;
     auto page_id = [&](const Cursor& c) -> int {
-        return sload_i32(a.page_table + static_cast<int64_t>(c.b) * a.max_pages + c.p);
+        return page_table[static_cast<int64_t>(c.b) * a.max_pages + c.p];
     };
     auto issue = [&](PageBuf<NW>& buf, int pid, int j) {
         const char* kbase = kvb + (gqa_kv_offset(pid, 0, j, 0, Hkv, kPage, D)) * EB + lane_off;

@@ -145,6 +145,27 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 }
 
+// Start the scalar read of *next_pid, wait until at most N vector memory
+// operations of this wave are outstanding (the chunk about to be computed has
+// landed), then meet the workgroup at a barrier.  The page-id read overlaps
+// the wait for the chunk instead of stalling the wave on its own.
+template <int N>
+__device__ __forceinline__ int wait_chunk_barrier(const int32_t* next_pid) {
+    int v;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt vmcnt(%2)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier"
+                 : "=s"(v)
+                 : "s"(next_pid), "n"(N)
+                 : "memory");
+    return v;
+}
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+
+// Transposing 8-byte LDS read (gfx950): see the value-operand note in the kernel.
+__device__ __forceinline__ short4v ds_read_tr16(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p));
+}
+
 __device__ __forceinline__ floatx16_t mfma32(bf16x8_t a, bf16x8_t b, floatx16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -199,8 +220,7 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
     Cursor lc;
     cursor_init(lc, sh, a.seq_lens, P);
     int issued = 0;                                             // chunks issued so far
-    auto issue_chunk = [&]() {
-        const int pid = sload_i32(a.page_table + static_cast<int64_t>(lc.b) * a.max_pages + lc.p);
+    auto issue_chunk = [&](int pid) {
         int ln = lane;
         asm volatile("" : "+v"(ln));      // recomputed per chunk rather than held in a register
         const int dma_off = ((ln & 31) ^ (((2 * (w & 1) + (ln >> 5)) & 3) << 2)) * kRowBytes + (ln >> 5) * 16;
@@ -218,10 +238,17 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
     // ---- per-lane LDS offsets
     // score operand: token tb*16 + l16, block x = 4 kb + q4l (x & 3 = q4l)
     const int s_base = q4l * 512 + ((l16 ^ (q4l << 2)) << 4);
-    // value gathers: token kb*16 + 8 half + i, dim 64 w + 32 db + l32
-    const int gsw = (l32 >> 3) << 2;                            // 4 (x & 3) of this lane's dims
-    const int gbase = ((kDW / 8) * w + (l32 >> 3)) * 512 + (l32 & 7) * 2;
-    const int gx = (8 * half) ^ gsw;                            // block index of token 8 half (swizzled)
+    // value operand by transposing reads (ds_read_b64_tr_b16): in each group of
+    // 16 lanes, lane 4a+e receives element e of the 8-byte rows addressed by
+    // lanes a, 4+a, 8+a, 12+a.  Lane s of group G therefore addresses dims
+    // 16 (G & 1) + 4 (s & 3) .. +3 of token 8 (G >> 1) + (s >> 2) (+4 for the
+    // second read), so that lane l ends up with tokens 8 (l / 32) + j of dim
+    // l % 32, the B operand of the 32x32x16 product.
+    const int tr_s = lane & 15, tr_g = lane >> 4;
+    const int tr_x = 2 * (tr_g & 1) + ((tr_s >> 1) & 1);       // block within the 32 dims (x & 3)
+    const int tr_t = (8 * (tr_g >> 1) + (tr_s >> 2)) ^ (4 * tr_x);   // swizzled token position
+    const int tr_base = (kDW / 8) * w * 512 + tr_x * 512 + tr_t * 16 + 8 * (tr_s & 1);
+    const int tr_base2 = tr_base + ((tr_x & 1) ? -64 : 64);    // tokens + 4 (position bit 2 flips)
     const int pr_base = l32 * kPRow + half * 16;                // P operand of the value product
     const int hw = w * kHW;                                     // this wave's score heads (local)
     const int pw_base = (hw + l16) * kPRow + q4l * 8;           // P row written by this lane
@@ -262,9 +289,10 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
     int i = 0;                            // chunk index within the share
 
     // prologue: three chunks in flight
+    auto next_pid_addr = [&]() { return a.page_table + static_cast<int64_t>(lc.b) * a.max_pages + lc.p; };
 #pragma unroll
     for (int c = 0; c < kSlots - 1; ++c)
-        if (lc.k < n) issue_chunk();
+        if (lc.k < n) issue_chunk(sload_i32(next_pid_addr()));
 
     // Outer loop over the pieces of the share (one request each), inner loop
     // over a piece's chunks: the query slice is live only inside a piece.
@@ -273,17 +301,16 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
         reset();
         bool stream_end = false, share_end = false;
         for (;; ++i) {
-            // chunk i has landed once this wave's later loads are the only ones pending
+            // chunk i has landed once this wave's later loads are the only ones
+            // pending; B1: chunk i visible to all, chunk i-1 done by all.  The
+            // page id of the next chunk to load is read meanwhile.
             const int after = issued - 1 - i;
-            if (after >= 2) {
-                if (nq == 5) wait_vmcnt<10>(); else wait_vmcnt<8>();
-            } else if (after == 1) {
-                if (nq == 5) wait_vmcnt<5>(); else wait_vmcnt<4>();
-            } else {
-                wait_vmcnt<0>();
-            }
-            lds_barrier();                                      // B1: chunk i visible; chunk i-1 done
-            if (lc.k < n) issue_chunk();                        // into the slot chunk i-1 used
+            const int32_t* pa = next_pid_addr();                // valid even past the share's end
+            int pid;
+            if (after >= 2) pid = nq == 5 ? wait_chunk_barrier<10>(pa) : wait_chunk_barrier<8>(pa);
+            else if (after == 1) pid = nq == 5 ? wait_chunk_barrier<5>(pa) : wait_chunk_barrier<4>(pa);
+            else pid = wait_chunk_barrier<0>(pa);
+            if (lc.k < n) issue_chunk(pid);                     // into the slot chunk i-1 used
 
             char* slot = sm.ring[i % kSlots];
             const int nvalid = min(kMlaChunk, cc.len - cc.p * P - cc.ci * kMlaChunk);
@@ -388,16 +415,9 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
                     aop[hb] = *reinterpret_cast<const bf16x8_t*>(sm.p + pr_base + hb * 32 * kPRow + kb * 32);
 #pragma unroll
                 for (int db = 0; db < 2; ++db) {
-                    uint32_t wv[4];
-#pragma unroll
-                    for (int i2 = 0; i2 < 4; ++i2) {
-                        const uint32_t lo = *reinterpret_cast<const uint16_t*>(
-                            slot + gbase + ((gx ^ (2 * i2)) << 4) + db * 2048 + kb * 256);
-                        const uint32_t hi = *reinterpret_cast<const uint16_t*>(
-                            slot + gbase + ((gx ^ (2 * i2 + 1)) << 4) + db * 2048 + kb * 256);
-                        wv[i2] = lo | (hi << 16);
-                    }
-                    const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3]));
+                    const short4v lo = ds_read_tr16(slot + tr_base + db * 2048 + kb * 256);
+                    const short4v hi = ds_read_tr16(slot + tr_base2 + db * 2048 + kb * 256);
+                    const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
                     for (int hb = 0; hb < nhb; ++hb) acc[hb][db] = mfma32(aop[hb], bop, acc[hb][db]);
                 }
