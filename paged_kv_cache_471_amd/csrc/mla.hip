@@ -161,6 +161,27 @@ __device__ __forceinline__ int wait_chunk_barrier(const int32_t* next_pid) {
 
 typedef short short4v __attribute__((ext_vector_type(4)));
 
+// Reductions over the lane pairs (l, l ^ 16) and (l, l ^ 32) with the gfx950
+// row swaps: after swapping a value with itself, the two results hold the
+// values of both lanes of each pair, in one order or the other, so max and
+// sum of the two are the pairwise max and sum (no LDS round trip).
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Transposing 8-byte LDS read (gfx950): see the value-operand note in the kernel.
 __device__ __forceinline__ short4v ds_read_tr16(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p));
@@ -364,8 +385,7 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
                 }
 #pragma unroll
                 for (int r = 0; r < 8; ++r) cmax = fmaxf(cmax, sv[r]);
-                cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-                cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+                cmax = max_xor32(max_xor16(cmax));
                 const float m_new = cmax > m_run + kRaise ? cmax : m_run;
                 const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
                 float psum = 0.0f;
@@ -381,8 +401,7 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
                     }
                     *reinterpret_cast<uint2*>(sm.p + pw_base + tb * 32) = make_uint2(pk[0], pk[1]);
                 }
-                psum += __shfl_xor(psum, 16, 64);
-                psum += __shfl_xor(psum, 32, 64);
+                psum = sum_xor32(sum_xor16(psum));
                 l_run = __builtin_fmaf(l_run, alpha, psum);
                 m_run = m_new;
                 if (lane < 16) sm.alpha[hw + l16] = alpha;
