@@ -24,12 +24,16 @@
 //    32 x + (t ^ 4 (x & 3)).  Each 1 KiB load then copies a fixed per-lane
 //    pattern, an MFMA operand read of 16 or 32 tokens covers whole bank rows,
 //    and the column gathers of the value product fall on different banks.
-//  * Scores: wave w owns heads [16w, 16w+16).  Its query slice (18 K-blocks
-//    of 32) stays in registers as the B operand of v_mfma_f32_16x16x32_bf16;
-//    latent rows are the A operand, so S^T [16 tokens x 16 heads] comes out
-//    with each lane holding 4 tokens of one head; the two 16-token blocks of
-//    a chunk are two independent MFMA chains.  Operands are read two
-//    K-blocks ahead of their MFMAs.
+//  * Scores: waves 2j and 2j+1 share heads [32j, 32j+32) and split the
+//    latent: wave w takes latent half w & 1 (9 K-blocks of 32).  Its query
+//    slice (2 head blocks x 9 K-blocks) stays in registers as the B operand
+//    of v_mfma_f32_16x16x32_bf16; latent rows are the A operand, so partial
+//    S^T [16 tokens x 16 heads] tiles come out with each lane holding 4
+//    tokens of one head.  Every latent row is thus read from LDS by four
+//    waves, not eight.  Wave w keeps the tiles of heads [16w, 16w+16) and
+//    hands the other head block to its partner through LDS; after one
+//    barrier each wave adds the partner's half and owns its 16 heads.
+//    Operands are read two K-blocks ahead of their MFMAs.
 //  * Softmax: per head a running maximum (base 2, log2(e) folded into the
 //    scale) that is only raised when a chunk's maximum exceeds it by more
 //    than 8, so weights stay <= 2^8 and the value rows rarely need rescaling.
@@ -60,11 +64,13 @@ constexpr int kRowBytes = kMlaLatent * 2;             // 1152 bytes per token in
 constexpr int kXB = kRowBytes / 16;                   // 72 16-byte blocks per token
 constexpr int kSlotBytes = kXB * kMlaChunk * 16;      // 36864
 constexpr int kSlotLoads = kSlotBytes / 1024;         // 36 wave-wide 16-byte loads
-constexpr int kMaxLoadsPerWave = (kSlotLoads + kWaves - 1) / kWaves;   // 5
+constexpr int kLoaders = 4;                           // waves that issue the chunk loads
+constexpr int kLoadsPerLoader = kSlotLoads / kLoaders;   // 9
+static_assert(kSlotLoads % kLoaders == 0 && kLoaders % 2 == 0, "loader split");
 constexpr int kSlots = 4;
 constexpr int kHG = kMlaMaxHeads;                     // heads per workgroup
 constexpr int kPRow = 80;                             // bytes per head row of P (64 + 16 pad)
-constexpr int kSKB = kMlaLatent / 32;                 // 18 K-blocks of the score product
+constexpr int kSKB = kMlaLatent / 64;                 // 9 K-blocks of 32 per latent half
 constexpr int kHW = 16;                               // score heads per wave
 constexpr int kDW = kMlaV / kWaves;                   // 64 value dims per wave
 constexpr float kRaise = 8.0f;                        // running max moves only past this margin
@@ -72,13 +78,23 @@ constexpr int kPD = 2;                                // score operand reads in 
 
 static_assert(kHG == kWaves * kHW, "each wave owns 16 score heads");
 
+// Per-wave area of 2 KiB, used in turn by
+//  * the partner's partial scores for this wave's heads (8 floats per lane),
+//    written before and read after the mid-chunk barrier, then by
+//  * P rows of the wave's 16 heads (80 bytes each), their rescale factors,
+//    the wave's rescale flag and, at the end of a piece, the final sums.
+// Every use of one kind ends before the next chunk's first barrier.
+constexpr int kArea = 2048;
+constexpr int kAlphaOff = kHW * kPRow;                // 1280
+constexpr int kFinOff = kAlphaOff + kHW * 4;          // 1344
+constexpr int kFlagOff = kFinOff + kHW * 4;           // 1408
+static_assert(kFlagOff + 4 <= kArea && 2 * 64 * 16 == kArea, "area layout");
+
 struct __align__(16) Smem {
     char ring[kSlots][kSlotBytes];
-    char p[kHG * kPRow];
-    float alpha[kHG];
-    float fin_l[kHG];
-    int flags[kWaves];
+    char area[kWaves][kArea];
 };
+static_assert(sizeof(Smem) <= 160 * 1024, "LDS");
 
 // Compute/load cursor over the chunks of a worker's share.  Wave-uniform.
 struct Cursor {
@@ -203,10 +219,6 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
     __shared__ Smem sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int half = lane >> 5;
-    const int l32 = lane & 31;
-    const int l16 = lane & 15;
-    const int q4l = (lane >> 4) & 3;                  // lane group of 16
     const int w = uniform(tid >> 6);
     const int g = blockIdx.x % a.workers;             // worker
     const int hs = blockIdx.x / a.workers;            // head half
@@ -228,64 +240,113 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
     if (g >= A) return;
     const int n = static_cast<int>(sh.c1 - sh.c0);
 
-    // ---- LDS set-up: P rows of absent heads stay zero, their alpha one.
-    for (int i = tid; i < kHG * kPRow / 4; i += kBlock) reinterpret_cast<int*>(sm.p)[i] = 0;
-    for (int i = tid; i < kHG; i += kBlock) sm.alpha[i] = 1.0f;
-    if (tid < kWaves) sm.flags[tid] = 0;
+    // ---- LDS set-up: P rows of absent heads stay zero, their alpha one, and
+    //      every flag zero (areas of absent heads are never written again).
+    char* const xa = &sm.area[0][0];
+    for (int i = tid; i < kWaves * kArea / 4; i += kBlock) {
+        const int off = (4 * i) % kArea;
+        reinterpret_cast<float*>(xa)[i] = off >= kAlphaOff && off < kFinOff ? 1.0f : 0.0f;
+    }
 
-    // ---- chunk loader: wave w issues loads q = w + 8 i (5 loads for w < 4,
-    //      4 otherwise); load q fills positions [64 q, 64 q + 64): x = 2 q +
-    //      half, t' = l32, source token t = t' ^ 4 ((2 q + half) & 3), and
-    //      (2 q) & 3 = 2 (w & 1) for every i.
-    const int nq = (kSlotLoads - w + kWaves - 1) / kWaves;
+    // ---- chunk loader: waves 0-3 issue loads q = w + 4 i (9 each).  Two waves
+    //      share each SIMD and the first four get ahead of the other four
+    //      (they wait at the barriers), so the loads go on their side.  Load q
+    //      fills positions [64 q, 64 q + 64): x = 2 q + half, t' = l32, source
+    //      token t = t' ^ 4 ((2 q + half) & 3), and (2 q) & 3 = 2 (w & 1) for
+    //      every i.
+    const bool loader = w < kLoaders;
     Cursor lc;
     cursor_init(lc, sh, a.seq_lens, P);
     int issued = 0;                                             // chunks issued so far
-    auto issue_chunk = [&](int pid) {
+    // source of this lane's part of the next chunk to load (page pid)
+    auto dma_src = [&](int pid) {
         int ln = lane;
         asm volatile("" : "+v"(ln));      // recomputed per chunk rather than held in a register
         const int dma_off = ((ln & 31) ^ (((2 * (w & 1) + (ln >> 5)) & 3) << 2)) * kRowBytes + (ln >> 5) * 16;
-        const char* src = kvb + (static_cast<int64_t>(pid) * P + lc.ci * kMlaChunk) * kRowBytes + dma_off;
-        const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)sm.ring[issued % kSlots]));
-#pragma unroll
-        for (int i = 0; i < kMaxLoadsPerWave; ++i) {
-            const int q = w + kWaves * i;
-            if (i < nq) lds_dma16(src + 32 * q, lds_base + q * 1024);
-        }
+        return kvb + (static_cast<int64_t>(pid) * P + lc.ci * kMlaChunk) * kRowBytes + dma_off;
+    };
+    auto dma_lds = [&]() {
+        return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)sm.ring[issued % kSlots]));
+    };
+    // load j (0..8) of this loader wave's share of the chunk
+    auto dma_load = [&](const char* src, uint32_t lds_base, int j) {
+        const int q = w + kLoaders * j;
+        lds_dma16(src + 32 * q, lds_base + q * 1024);
+    };
+    auto chunk_issued = [&]() {
         ++issued;
         cursor_next(lc, a.seq_lens, P, n);
     };
+    auto issue_chunk = [&](int pid) {
+        if (loader) {
+            const char* src = dma_src(pid);
+            const uint32_t lds_base = dma_lds();
+#pragma unroll
+            for (int j = 0; j < kLoadsPerLoader; ++j) dma_load(src, lds_base, j);
+        }
+        chunk_issued();
+    };
 
-    // ---- per-lane LDS offsets
+    // ---- per-lane LDS offsets.  They are recomputed inside the chunk loop from
+    //      a lane index passed through an opaque move, so that the compiler does
+    //      not keep them all in registers across the loop (registers are full
+    //      with the query slice and the value accumulators).
+    auto fresh_lane = [&]() {
+        int l = lane;
+        asm volatile("" : "+v"(l));
+        return l;
+    };
     // score operand: token tb*16 + l16, block x = 4 kb + q4l (x & 3 = q4l)
-    const int s_base = q4l * 512 + ((l16 ^ (q4l << 2)) << 4);
+    auto s_base_of = [](int ln) {
+        const int q4 = (ln >> 4) & 3;
+        return q4 * 512 + (((ln & 15) ^ (q4 << 2)) << 4);
+    };
     // value operand by transposing reads (ds_read_b64_tr_b16): in each group of
     // 16 lanes, lane 4a+e receives element e of the 8-byte rows addressed by
     // lanes a, 4+a, 8+a, 12+a.  Lane s of group G therefore addresses dims
     // 16 (G & 1) + 4 (s & 3) .. +3 of token 8 (G >> 1) + (s >> 2) (+4 for the
     // second read), so that lane l ends up with tokens 8 (l / 32) + j of dim
-    // l % 32, the B operand of the 32x32x16 product.
-    const int tr_s = lane & 15, tr_g = lane >> 4;
-    const int tr_x = 2 * (tr_g & 1) + ((tr_s >> 1) & 1);       // block within the 32 dims (x & 3)
-    const int tr_t = (8 * (tr_g >> 1) + (tr_s >> 2)) ^ (4 * tr_x);   // swizzled token position
-    const int tr_base = (kDW / 8) * w * 512 + tr_x * 512 + tr_t * 16 + 8 * (tr_s & 1);
-    const int tr_base2 = tr_base + ((tr_x & 1) ? -64 : 64);    // tokens + 4 (position bit 2 flips)
-    const int pr_base = l32 * kPRow + half * 16;                // P operand of the value product
-    const int hw = w * kHW;                                     // this wave's score heads (local)
-    const int pw_base = (hw + l16) * kPRow + q4l * 8;           // P row written by this lane
-    const bool s_active = hw < HG;
+    // l % 32, the B operand of the 32x32x16 product.  Returns the first
+    // read's offset; the second one's differs by +-64 (position bit 2 flips).
+    auto tr_base_of = [&](int ln, int& second) {
+        const int s16 = ln & 15, gg = ln >> 4;
+        const int x = 2 * (gg & 1) + ((s16 >> 1) & 1);          // block within the 32 dims (x & 3)
+        const int t = (8 * (gg >> 1) + (s16 >> 2)) ^ (4 * x);    // swizzled token position
+        const int base = (kDW / 8) * w * 512 + x * 512 + t * 16 + 8 * (s16 & 1);
+        second = base + ((x & 1) ? -64 : 64);
+        return base;
+    };
+    // P of head h sits in area h / 16, row h % 16; operand rows hb*32 + l32
+    auto pr_base_of = [](int ln) { return ((ln >> 4) & 1) * kArea + (ln & 15) * kPRow + (ln >> 5) * 16; };
+    const int hw = w * kHW;                                     // this wave's softmax heads (local)
+    const bool s_active = hw < HG;                              // owns live heads
+    // Score head blocks by role: slot 0 = this wave's own heads [16w, 16w+16),
+    // slot 1 = the partner's.  With 16 heads in all (one block), both waves of
+    // pair 0 compute heads [0, 16) in slot 0 and wave 1 hands its half over.
+    constexpr int NQB = HG >= 32 ? 2 : 1;                       // head blocks of a score wave
+    const int hg = w >> 1;                                      // 32-head group of the pair
+    const int lh = w & 1;                                       // latent half
+    const bool c_active = 32 * hg < HG;                         // computes partial scores
+    const bool sends = NQB == 2 || lh == 1;                     // hands a block to the partner
     const int dw = w * kDW;                                     // this wave's value dims
 
-    bf16x8_t qreg[kSKB];
+    bf16x8_t qreg[NQB][kSKB];
     float m_run = kMaxInit, l_run = 0.0f;
     floatx16_t acc[nhb][2];
 
     auto load_q = [&](int b) {
-        if (!s_active) return;
-        const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(
-            static_cast<const uint16_t*>(a.q) + (static_cast<int64_t>(b) * H + h0 + hw + l16) * kMlaLatent + 8 * q4l);
+        if (!c_active) return;
+        const int ln = fresh_lane();
+        const int l16 = ln & 15, q4l = (ln >> 4) & 3;
 #pragma unroll
-        for (int kb = 0; kb < kSKB; ++kb) qreg[kb] = src[kb * 4];
+        for (int hb = 0; hb < NQB; ++hb) {
+            const int hq = NQB == 1 ? 0 : 16 * (hb == 0 ? w : w ^ 1);
+            const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(
+                static_cast<const uint16_t*>(a.q) + (static_cast<int64_t>(b) * H + h0 + hq + l16) * kMlaLatent +
+                lh * (kMlaLatent / 2) + 8 * q4l);
+#pragma unroll
+            for (int kb = 0; kb < kSKB; ++kb) qreg[hb][kb] = src[kb * 4];
+        }
         // Let the compiler see these loads complete here (this also drains the
         // chunk ring, once per piece): otherwise it would keep them pending
         // around the loop and wait on the ring's loads inside the score product.
@@ -328,10 +389,20 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
             const int after = issued - 1 - i;
             const int32_t* pa = next_pid_addr();                // valid even past the share's end
             int pid;
-            if (after >= 2) pid = nq == 5 ? wait_chunk_barrier<10>(pa) : wait_chunk_barrier<8>(pa);
-            else if (after == 1) pid = nq == 5 ? wait_chunk_barrier<5>(pa) : wait_chunk_barrier<4>(pa);
+            if (after >= 2) pid = loader ? wait_chunk_barrier<2 * kLoadsPerLoader>(pa) : wait_chunk_barrier<0>(pa);
+            else if (after == 1) pid = loader ? wait_chunk_barrier<kLoadsPerLoader>(pa) : wait_chunk_barrier<0>(pa);
             else pid = wait_chunk_barrier<0>(pa);
-            if (lc.k < n) issue_chunk(pid);                     // into the slot chunk i-1 used
+            // The loads of chunk i+3 (into the slot chunk i-1 used) are spread
+            // over the score product: a wave that issues them in one burst
+            // waits while the memory pipeline takes each 1 KiB load in turn.
+            const bool more = lc.k < n;
+            const bool dma = loader && more;
+            const char* dsrc = dma ? dma_src(pid) : nullptr;
+            const uint32_t dlds = dma_lds();
+            if (dma && !c_active) {
+#pragma unroll
+                for (int j = 0; j < kLoadsPerLoader; ++j) dma_load(dsrc, dlds, j);
+            }
 
             char* slot = sm.ring[i % kSlots];
             const int nvalid = min(kMlaChunk, cc.len - cc.p * P - cc.ci * kMlaChunk);
@@ -345,12 +416,16 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
                 }
             }
 
-            // ---- scores and softmax for this wave's 16 heads
-            if (s_active) {
+            // ---- partial scores: heads [32 hg, 32 hg + 32) (slots by role), latent half lh
+            floatx4_t sacc[2][NQB];
+            if (c_active) {
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                    for (int hb = 0; hb < NQB; ++hb) sacc[tb][hb] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
                 // operands are read kPD K-blocks ahead of their MFMAs
-                floatx4_t s0 = {}, s1 = {};
                 bf16x8_t c0[kPD], c1[kPD];
-                const char* sp = slot + s_base;
+                const char* sp = slot + s_base_of(fresh_lane()) + lh * (kSKB * 2048);
 #pragma unroll
                 for (int d = 0; d < kPD; ++d) {
                     c0[d] = *reinterpret_cast<const bf16x8_t*>(sp + d * 2048);
@@ -363,17 +438,40 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
                         c0[kb % kPD] = *reinterpret_cast<const bf16x8_t*>(sp + (kb + kPD) * 2048);
                         c1[kb % kPD] = *reinterpret_cast<const bf16x8_t*>(sp + (kb + kPD) * 2048 + 256);
                     }
-                    s0 = mfma16(a0, qreg[kb], s0);
-                    s1 = mfma16(a1, qreg[kb], s1);
+#pragma unroll
+                    for (int hb = 0; hb < NQB; ++hb) {
+                        sacc[0][hb] = mfma16(a0, qreg[hb][kb], sacc[0][hb]);
+                        sacc[1][hb] = mfma16(a1, qreg[hb][kb], sacc[1][hb]);
+                    }
+                    static_assert(kSKB == kLoadsPerLoader, "one chunk load per K-block");
+                    if (dma) dma_load(dsrc, dlds, kb);
                 }
                 // keep the order written above: the first reads, then per K-block
-                // two MFMAs followed by the next two reads
+                // the MFMAs followed by the next two reads
                 __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPD, 0);
 #pragma unroll
                 for (int kb = 0; kb < kSKB; ++kb) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NQB, 0);
                     if (kb + kPD < kSKB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                 }
+                // the partner's head block goes to the partner's area
+                if (sends) {
+                    char* dst = xa + (w ^ 1) * kArea + lane * 16;
+#pragma unroll
+                    for (int tb = 0; tb < 2; ++tb) *reinterpret_cast<floatx4_t*>(dst + tb * 1024) = sacc[tb][NQB - 1];
+                }
+            }
+            if (more) chunk_issued();
+            lds_barrier();                                      // partial scores exchanged
+
+            // ---- softmax for this wave's 16 heads
+            if (s_active) {
+                const int ln = fresh_lane();
+                const int q4l = (ln >> 4) & 3, l16 = ln & 15;
+                const int pw_base = w * kArea + l16 * kPRow + q4l * 8;   // P row written by this lane
+                const char* src = xa + w * kArea + ln * 16;
+                const floatx4_t s0 = sacc[0][0] + *reinterpret_cast<const floatx4_t*>(src);
+                const floatx4_t s1 = sacc[1][0] + *reinterpret_cast<const floatx4_t*>(src + 1024);
                 // lane holds S^T[token tb*16 + 4 q4l + r][head hw + l16]
                 float sv[8];
                 float cmax = -__builtin_inff();
@@ -399,24 +497,30 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
                         psum += p0 + p1;
                         pk[r >> 1] = f32_to_bf16_bits(p0) | (static_cast<uint32_t>(f32_to_bf16_bits(p1)) << 16);
                     }
-                    *reinterpret_cast<uint2*>(sm.p + pw_base + tb * 32) = make_uint2(pk[0], pk[1]);
+                    *reinterpret_cast<uint2*>(xa + pw_base + tb * 32) = make_uint2(pk[0], pk[1]);
                 }
                 psum = sum_xor32(sum_xor16(psum));
                 l_run = __builtin_fmaf(l_run, alpha, psum);
                 m_run = m_new;
-                if (lane < 16) sm.alpha[hw + l16] = alpha;
+                if (lane < 16) *reinterpret_cast<float*>(xa + w * kArea + kAlphaOff + 4 * l16) = alpha;
                 const bool moved = __ballot(alpha != 1.0f) != 0ull;
-                if (lane == 0) sm.flags[w] = moved;
+                if (lane == 0) *reinterpret_cast<int*>(xa + w * kArea + kFlagOff) = moved;
             }
             lds_barrier();                                      // B2: P, alpha and flags visible
 
             // ---- value update for dims [dw, dw + 64) of every head
+            const int oln = fresh_lane();
+            const int ohalf = oln >> 5;
 #pragma unroll
             for (int hb = 0; hb < nhb; ++hb) {
-                if ((sm.flags[2 * hb] | sm.flags[2 * hb + 1]) == 0) continue;
+                const int f0 = *reinterpret_cast<const int*>(xa + (2 * hb) * kArea + kFlagOff);
+                const int f1 = *reinterpret_cast<const int*>(xa + (2 * hb + 1) * kArea + kFlagOff);
+                if ((f0 | f1) == 0) continue;
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
-                    const float4 al = *reinterpret_cast<const float4*>(&sm.alpha[hb * 32 + q4 * 8 + 4 * half]);
+                    // heads hb*32 + 8 q4 + 4 half .. +3: area 2 hb + q4 / 2
+                    const float4 al = *reinterpret_cast<const float4*>(
+                        xa + (2 * hb + (q4 >> 1)) * kArea + kAlphaOff + 4 * ((q4 & 1) * 8 + 4 * ohalf));
 #pragma unroll
                     for (int db = 0; db < 2; ++db) {
                         acc[hb][db][q4 * 4 + 0] *= al.x;
@@ -426,12 +530,15 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
                     }
                 }
             }
+            int tr_base2;
+            const int tr_base = tr_base_of(oln, tr_base2);
+            const int pr_base = pr_base_of(oln);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 bf16x8_t aop[nhb];
 #pragma unroll
                 for (int hb = 0; hb < nhb; ++hb)
-                    aop[hb] = *reinterpret_cast<const bf16x8_t*>(sm.p + pr_base + hb * 32 * kPRow + kb * 32);
+                    aop[hb] = *reinterpret_cast<const bf16x8_t*>(xa + pr_base + hb * 2 * kArea + kb * 32);
 #pragma unroll
                 for (int db = 0; db < 2; ++db) {
                     const short4v lo = ds_read_tr16(slot + tr_base + db * 2048 + kb * 256);
@@ -455,7 +562,8 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
         const int b = cc.b;
         const int slot_id = first_piece ? g : A + g;
         if (s_active && lane < 16) {
-            sm.fin_l[hw + l16] = l_run;
+            const int l16 = fresh_lane();
+            *reinterpret_cast<float*>(xa + w * kArea + kFinOff + 4 * l16) = l_run;
             const float lse2 = m_run + __builtin_log2f(l_run);
             const int h = h0 + hw + l16;
             if (whole) {
@@ -481,7 +589,8 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
                     for (int r4 = 0; r4 < 4; ++r4) {
                         const int hl = hb * 32 + q4 * 8 + 4 * ehalf + r4;
                         if (HG % 32 != 0 && hl >= HG) continue;
-                        const float inv = __builtin_amdgcn_rcpf(sm.fin_l[hl]);
+                        const float inv = __builtin_amdgcn_rcpf(
+                            *reinterpret_cast<const float*>(xa + (hl >> 4) * kArea + kFinOff + 4 * (hl & 15)));
 #pragma unroll
                         for (int db = 0; db < 2; ++db)
                             dst[hl * kMlaV + db * 32] = f32_to_bf16_bits(acc[hb][db][q4 * 4 + r4] * inv);
@@ -496,7 +605,8 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
                     for (int r4 = 0; r4 < 4; ++r4) {
                         const int hl = hb * 32 + q4 * 8 + 4 * ehalf + r4;
                         if (HG % 32 != 0 && hl >= HG) continue;
-                        const float inv = __builtin_amdgcn_rcpf(sm.fin_l[hl]);
+                        const float inv = __builtin_amdgcn_rcpf(
+                            *reinterpret_cast<const float*>(xa + (hl >> 4) * kArea + kFinOff + 4 * (hl & 15)));
 #pragma unroll
                         for (int db = 0; db < 2; ++db) dst[hl * kMlaV + db * 32] = acc[hb][db][q4 * 4 + r4] * inv;
                     }
@@ -509,7 +619,7 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
             const int gl = last_worker_of(start + cc.pages, sh.W, A);
             a.stream_info[b] = make_int2(static_cast<int>(start), gl - gf + 1);
         }
-        __syncthreads();                                        // fin_l reused by the next piece
+        __syncthreads();                                        // final sums read before areas are reused
         cursor_next(cc, a.seq_lens, P, n);
         first_piece = false;
         piece_p0 = 0;
