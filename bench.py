@@ -196,23 +196,27 @@ def _to_dev(x, dtype, dev):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to(dev).view(torch.float8_e4m3fn)
 
 
-SECONDARY_WARM_S = 0.3          # untimed stepping before each secondary workload is timed
+SETTLE_S = 0.3                  # untimed stepping before a workload's warmup steps (see time_runner)
 
 
 def time_runner(runner, steps, warmup, kernel_timer=True, warm_s=0.0):
-    """Run `warmup` untimed steps (then keep stepping untimed until `warm_s`
-    seconds have passed, if given), then time exactly `steps` steps."""
+    """Settle, run `warmup` untimed steps, then time exactly `steps` steps.
+
+    Settling (if warm_s > 0) steps the workload untimed for warm_s seconds
+    first: the inputs were just generated on the host with the GPU idle, and a
+    decode server steps back to back, so the timed steps should see the clock
+    the GPU settles at under this load, not its ramp from idle."""
     import torch
     import paged_kv_cache_471_amd as da
-    for _ in range(warmup):
-        runner.step()
-    torch.cuda.synchronize()
     if warm_s > 0:
         t_end = time.perf_counter() + warm_s
         while time.perf_counter() < t_end:
             for _ in range(8):
                 runner.step()
             torch.cuda.synchronize()
+    for _ in range(warmup):
+        runner.step()
+    torch.cuda.synchronize()
     if kernel_timer:
         da.timer_begin(steps)
     start = torch.cuda.Event(enable_timing=True)
@@ -293,7 +297,7 @@ def main():
         print(json.dumps({"mode": "step", "workload": cfg.name, "ms_per_step": ms}))
         return
 
-    ms, kms, wall = time_runner(runner, args.steps, args.warmup)
+    ms, kms, wall = time_runner(runner, args.steps, args.warmup, warm_s=SETTLE_S)
     headline_case = runner.case
     gbs = runner.bytes / (ms * 1e-3) / 1e9
     kern_gbs = runner.bytes / (kms * 1e-3) / 1e9 if kms else None
@@ -338,10 +342,7 @@ def main():
         runner2 = make_runner(scfg)
         print(f"# secondary {name}: sum L = {runner2.tokens}, {runner2.bytes / 1e6:.1f} MB", file=sys.stderr,
               flush=True)
-        # The inputs were just generated on the host with the GPU idle: step it
-        # for a fixed time first so that the timed steps run at a settled clock.
-        sms, skms, _ = time_runner(runner2, max(10, args.steps // 2), max(3, args.warmup // 2),
-                                   warm_s=SECONDARY_WARM_S)
+        sms, skms, _ = time_runner(runner2, max(10, args.steps // 2), max(3, args.warmup // 2), warm_s=SETTLE_S)
         sg = runner2.bytes / (sms * 1e-3) / 1e9
         entry = {"workload": workload_desc(scfg), "ms_per_step": sms, "GBps": round(sg, 2),
                  "pct_hbm_peak": round(100 * sg / HBM_PEAK_GBS, 2),
