@@ -293,7 +293,7 @@ def main():
     print(f"# headline {cfg.name}: inputs generated in {runner.gen_s:.1f}s, "
           f"sum L = {runner.tokens}, {runner.bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
     if args.mode == "step":
-        ms, kms, _ = time_runner(runner, args.steps, args.warmup, kernel_timer=False)
+        ms, kms, _ = time_runner(runner, args.steps, args.warmup, kernel_timer=False, warm_s=SETTLE_S)
         print(json.dumps({"mode": "step", "workload": cfg.name, "ms_per_step": ms}))
         return
 
