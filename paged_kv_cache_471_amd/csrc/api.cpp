@@ -345,7 +345,12 @@ int decode_attn_paged(const da_paged_desc* d, const void* q, const void* kv_page
     ma.units = d->num_kv_heads;
     ma.group = group;
     ma.dim = d->head_dim;
-    ma.heads_per_block = 1;
+    // Streams split into about two pieces or fewer are merged by one
+    // workgroup for all the heads of their group (fewer, fuller workgroups;
+    // most of them return at once); more deeply split streams by one
+    // workgroup per head, so that their pieces spread over more lanes.
+    const int pieces = ga.workers / (streams > 0 ? streams : 1);
+    ma.heads_per_block = pieces <= 2 && group * d->head_dim <= 4 * 256 ? group : 1;
     ma.out_is_bf16 = d->q_dtype == DA_BF16;
     e = da::launch_merge(ma, streams, s);
     if (e != hipSuccess) return hip_fail(e);

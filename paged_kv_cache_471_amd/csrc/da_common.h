@@ -39,6 +39,16 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// a.x*b.x + a.y*b.y (the same operation with a zero addend).  The compiler
+// emits the accumulate-in-place encoding for dot2_bf16, which needs a move of
+// 0.0 into the destination first; the three-operand encoding takes the zero
+// as an inline constant.
+__device__ __forceinline__ float dot2_bf16_first(uint32_t a, uint32_t b) {
+    float r;
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // two OCP e4m3 codes (bytes 0,1 or 2,3 of w) -> packed bf16 pair (exact).
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {

@@ -41,6 +41,7 @@ namespace da {
 namespace {
 
 constexpr int kPage = 16;           // tokens per page this kernel is written for
+constexpr float kRaise = 8.0f;      // fp8: running max moves only past this margin (base 2)
 constexpr int kTPL = kPage / 4;     // tokens per lane per page
 
 template <int QT, int KV, int D, int GS>
@@ -238,9 +239,11 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
                 }
 #pragma unroll
                 for (int hh = 0; hh < GS; ++hh) {
-                    float t = 0.0f;
+                    // fp8 (arithmetic-bound): the zero-addend form saves a move per
+                    // score; bf16 keeps the builtin, which schedules better
+                    float t = KV == kFP8 ? dot2_bf16_first(qb[hh][0], kp[0]) : dot2_bf16(qb[hh][0], kp[0], 0.0f);
 #pragma unroll
-                    for (int w = 0; w < QW; ++w) t = dot2_bf16(qb[hh][w], kp[w], t);
+                    for (int w = 1; w < QW; ++w) t = dot2_bf16(qb[hh][w], kp[w], t);
                     s[hh][i] = t;
                 }
             }
@@ -260,13 +263,21 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
                 }
             }
         }
+        // Online softmax.  For fp8 K/V (arithmetic-bound) the maximum is raised
+        // lazily: m only moves when a page's maximum exceeds it by more than
+        // kRaise (base 2), so weights stay below 2^kRaise and the accumulators
+        // are rescaled only on the rare pages where some lane's maximum moved
+        // (a wave-uniform test).  The bandwidth-bound formats keep the plain
+        // update: the branches would cost more in load scheduling than the
+        // multiplies they save.
+        constexpr bool kLazy = KV == kFP8;
         float p[GS][kTPL];
 #pragma unroll
         for (int hh = 0; hh < GS; ++hh) {
             float mx = s[hh][0];
 #pragma unroll
             for (int i = 1; i < kTPL; ++i) mx = fmaxf(mx, s[hh][i]);
-            const float mn = fmaxf(m[hh], mx);
+            const float mn = kLazy ? (mx > m[hh] + kRaise ? mx : m[hh]) : fmaxf(m[hh], mx);
             const float alpha = __builtin_amdgcn_exp2f(m[hh] - mn);
 #pragma unroll
             for (int i = 0; i < kTPL; ++i) p[hh][i] = __builtin_amdgcn_exp2f(s[hh][i] - mn);
@@ -275,8 +286,10 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
             for (int i = 1; i < kTPL; ++i) sum += p[hh][i];
             m[hh] = mn;
             l[hh] = __builtin_fmaf(l[hh], alpha, sum);
+            if (!kLazy || __ballot(alpha != 1.0f) != 0ull) {
 #pragma unroll
-            for (int d = 0; d < DL; ++d) acc[hh][d] *= alpha;
+                for (int d = 0; d < DL; ++d) acc[hh][d] *= alpha;
+            }
         }
 #pragma unroll
         for (int i = 0; i < kTPL; ++i) {
