@@ -15,7 +15,9 @@ Printed: one JSON line with the metric (algorithmic KV GB/s), tokens/s, the
 dominant kernel's roofline (its own duration from hipExtLaunchKernel events
 recorded over the timed region), HBM traffic from committed rocprofv3 counter
 runs when they match the current kernel source, the float64 CPU oracle's
-throughput on a bounded sample, and the other workloads as secondary figures.
+throughput on a bounded sample, the other workloads as secondary figures, and
+the paged KV append (this step's K/V or latent written into its page slot)
+timed on the headline, MLA and fp8 workloads.
 """
 from __future__ import annotations
 
@@ -122,19 +124,20 @@ class GqaRunner:
         return int(self.case.seq_lens.astype("int64").sum())
 
     def oracle_sample(self, budget_s):
-        """Time the float64 oracle on requests in order until the budget is spent."""
+        """Time the float64 oracle on requests in order, passing over the batch
+        again and again, until the budget is spent."""
         import numpy as np
         import oracle
         from workloads import accounting
         c, cfg = self.case, self.cfg
+        B = len(c.seq_lens)
         done = []
         t0 = time.perf_counter()
-        for b in range(len(c.seq_lens)):
+        while time.perf_counter() - t0 < budget_s:
+            b = len(done) % B
             oracle.paged_decode_attention(c.q, cfg.q_dtype, c.kv, cfg.kv_dtype, c.page_table, c.seq_lens,
                                           cfg.page_size, c.scale, c.k_scale, c.v_scale, requests=[b])
             done.append(b)
-            if time.perf_counter() - t0 >= budget_s:
-                break
         dt = time.perf_counter() - t0
         lens = c.seq_lens[done]
         by = accounting.gqa_bytes(lens, cfg.page_size, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.q_dtype,
@@ -178,6 +181,57 @@ class MlaRunner:
     @property
     def tokens(self):
         return int(self.case.seq_lens.astype("int64").sum())
+
+
+class AppendRunner:
+    """This step's K/V (or MLA latent) written into the cache of an attention
+    runner's workload.  Each request writes its last history slot, which has
+    the bytes and the addressing of an append at the next position without
+    needing a fresh page."""
+
+    def __init__(self, attn):
+        import numpy as np
+        import torch
+        import workloads as wl
+        self.attn = attn
+        c, cfg = attn.case, attn.cfg
+        rng = np.random.default_rng(wl.BASE_SEED)
+        B = len(c.seq_lens)
+        self.pos = torch.from_numpy((c.seq_lens - 1).astype(np.int32)).cuda()
+        self.mla = isinstance(cfg, wl.MLAConfig)
+        if self.mla:
+            shape = (B, cfg.latent_dim)
+            self.new = [_to_dev(wl.to_bf16_bits(rng.standard_normal(shape).astype(np.float32)), wl.BF16, "cuda")]
+            self.bytes = B * cfg.latent_dim * 2 * 2 + 2 * B * 4
+            self.kv_dtype = wl.BF16
+        else:
+            shape = (B, cfg.kv_heads, cfg.head_dim)
+            self.new = [_to_dev(wl.to_bf16_bits(rng.standard_normal(shape).astype(np.float32)) if cfg.q_dtype == wl.BF16
+                                else rng.standard_normal(shape).astype(np.float32), cfg.q_dtype, "cuda")
+                        for _ in range(2)]
+            n = 2 * B * cfg.kv_heads * cfg.head_dim
+            self.bytes = n * (wl.ELEM_BYTES[cfg.q_dtype] + wl.ELEM_BYTES[cfg.kv_dtype]) + 2 * B * 4
+            self.kv_dtype = cfg.kv_dtype
+
+    def step(self):
+        import paged_kv_cache_471_amd as da
+        a = self.attn
+        if self.mla:
+            da.decode_kv_append_mla(self.new[0], a.kvs[0], a.pt, self.pos)
+        else:
+            da.decode_kv_append(self.new[0], self.new[1], a.kvs[0], a.pt, self.pos, k_scale=a.ks, v_scale=a.vs)
+
+
+def time_append(attn, steps, warmup, step_ms):
+    import workloads as wl
+    r = AppendRunner(attn)
+    ms, kms, _ = time_runner(r, steps, warmup, warm_s=0.1)
+    # ms_per_call is the rate at which the Python binding issues calls; the
+    # kernel itself is what a captured or native serving loop would pay.
+    return {"kv_dtype": "bf16" if r.mla else wl.DTYPE_NAMES[r.kv_dtype], "requests": attn.batch,
+            "ms_per_call": ms, "kernel_ms": kms, "algorithmic_bytes": r.bytes,
+            "kernel_GBps": round(r.bytes / (kms * 1e-3) / 1e9, 2) if kms else None,
+            "kernel_pct_of_attention_step": round(100 * kms / step_ms, 2) if kms else None}
 
 
 def make_runner(cfg):
@@ -268,8 +322,9 @@ def main():
                     help="comma list of other workloads to report beside the headline ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["bench", "copy", "step"], default="bench",
-                    help="copy: time a plain device copy; step: run the headline step only (for profilers)")
+    ap.add_argument("--mode", choices=["bench", "copy", "step", "append"], default="bench",
+                    help="copy: time a plain device copy; step: run the headline step only; append: run the "
+                         "workload's KV append only (both for profilers)")
     ap.add_argument("--copy-mb", type=int, default=1024)
     args = ap.parse_args()
 
@@ -296,9 +351,14 @@ def main():
         ms, kms, _ = time_runner(runner, args.steps, args.warmup, kernel_timer=False, warm_s=SETTLE_S)
         print(json.dumps({"mode": "step", "workload": cfg.name, "ms_per_step": ms}))
         return
+    if args.mode == "append":
+        ms, kms, _ = time_runner(AppendRunner(runner), args.steps, args.warmup, kernel_timer=False, warm_s=0.1)
+        print(json.dumps({"mode": "append", "workload": cfg.name, "ms_per_call": ms}))
+        return
 
     ms, kms, wall = time_runner(runner, args.steps, args.warmup, warm_s=SETTLE_S)
     headline_case = runner.case
+    appends = {cfg.name: time_append(runner, args.steps, args.warmup, ms)}
     gbs = runner.bytes / (ms * 1e-3) / 1e9
     kern_gbs = runner.bytes / (kms * 1e-3) / 1e9 if kms else None
     traffic = traffic_from_profiles()
@@ -356,9 +416,12 @@ def main():
             entry["mfma_TFLOPs"] = round(runner2.flops / (sms * 1e-3) / 1e12, 1)
             entry["pct_mfma_bf16_peak"] = round(100 * runner2.flops / (sms * 1e-3) / MFMA_BF16_PEAK, 2)
         secondary[name] = entry
+        if name in ("mla", "longfp8"):
+            appends[name] = time_append(runner2, max(10, args.steps // 2), max(3, args.warmup // 2), sms)
         runner = runner2
     if secondary:
         result["secondary"] = secondary
+    result["kv_append"] = appends
 
     if not args.no_cpu_baseline:
         import threadpoolctl
@@ -372,8 +435,9 @@ def main():
             "unit": "GB/s",
             "cores": 1,
             "kind": "oracle",
-            "sample": f"first {s['requests']} of {len(base.case.seq_lens)} requests of {cfg.name} "
-                      f"({s['tokens']} tokens, {s['seconds']:.1f} s), float64 numpy, BLAS limited to 1 thread",
+            "sample": f"{s['requests']} requests of {cfg.name} taken in order, cycling over its "
+                      f"{len(base.case.seq_lens)} ({s['tokens']} tokens, {s['seconds']:.1f} s), float64 numpy, "
+                      f"BLAS limited to 1 thread",
             "tokens_per_s": s["tokens"] / s["seconds"],
         }
     print(json.dumps(result), flush=True)

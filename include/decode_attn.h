@@ -155,6 +155,40 @@ int decode_attn_paged(const da_paged_desc* desc, const void* q, const void* kv_p
 int decode_attn_mla(const da_mla_desc* desc, const void* q, const void* kv_pages,
                     const int32_t* page_table, const int32_t* seq_lens, float scale,
                     void* out, float* lse, void* stream);
+/*
+ * decode_kv_append - write this step's new token into each request's paged
+ * history (the history grows by one token per decode step and is then read
+ * whole: Analytical Provisioning §2 and Fig. 1; paged KV-cache management:
+ * OpWeave §8; FP8 E4M3 KV with scales: SPLASH App. C.1 and App. B.1).
+ *   desc        host; the same description as decode_attn_paged; q_dtype is
+ *               the dtype of k_new and v_new.
+ *   k_new       device, [B][Hkv][D] q_dtype (16-byte aligned for fp32, 8 for bf16).
+ *   v_new       device, [B][Hkv][D] q_dtype.
+ *   kv_pages    device, [num_pages][2][Hkv][P][D] kv_dtype; for each request
+ *               with positions[b] = t >= 0 and each KV head j, the slot of
+ *               token t (page page_table[b][t / P], slot t % P) is written;
+ *               nothing else is touched.
+ *   page_table  device, int32 [B][max_pages_per_seq].
+ *   positions   device, int32 [B]: the token index of the new token (the
+ *               history length before this step); negative: no append.
+ *   stream      hipStream_t.
+ * Values: same dtype as the cache -> copied bit for bit.  bf16 into an fp8
+ * cache -> y = x / scale[j] computed in fp32, stored as the e4m3fn code
+ * nearest to y (ties to the even code), |y| > 448 saturating to +-448 and
+ * NaN stored as 0x7F (k_scale for K, v_scale for V).
+ * Data-dependent preconditions (t < max_pages_per_seq * P, the page ids
+ * read valid, no two requests writing one slot) are the caller's.
+ * Returns DA_OK or a negative status.
+ */
+int decode_kv_append(const da_paged_desc* desc, const void* k_new, const void* v_new, void* kv_pages,
+                     const int32_t* page_table, const int32_t* positions, void* stream);
+/*
+ * decode_kv_append_mla - the same for the absorbed-MLA cache: latent_new
+ * device bf16 [B][latent_dim] (16-byte aligned) is copied into slot t % P of
+ * page page_table[b][t / P] of kv_pages bf16 [num_pages][P][latent_dim].
+ */
+int decode_kv_append_mla(const da_mla_desc* desc, const void* latent_new, void* kv_pages,
+                         const int32_t* page_table, const int32_t* positions, void* stream);
 
 /*
  * decode_attn_plan - run the split-KV planner that the attention kernels

@@ -22,6 +22,7 @@ STATUS = {0: "DA_OK", -1: "DA_ERR_NULL", -2: "DA_ERR_SHAPE", -3: "DA_ERR_DTYPE",
           -5: "DA_ERR_WORKSPACE", -6: "DA_ERR_HIP"}
 
 EXPORTS = ("decode_attn_paged", "decode_attn_mla", "decode_attn_plan", "paged_kv_gather",
+           "decode_kv_append", "decode_kv_append_mla",
            "decode_attn_default_workers", "decode_attn_status_str", "decode_attn_last_hip_error",
            "decode_attn_timer_begin", "decode_attn_timer_end")
 
@@ -61,6 +62,10 @@ def _load():
     lib.decode_attn_plan.argtypes = [i32, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
     lib.decode_attn_plan.restype = ctypes.c_int
     lib.paged_kv_gather.argtypes = [ctypes.POINTER(PagedDesc), i32, vp, vp, vp, vp, vp]
+    lib.decode_kv_append.argtypes = [ctypes.POINTER(PagedDesc), vp, vp, vp, vp, vp, vp]
+    lib.decode_kv_append.restype = ctypes.c_int
+    lib.decode_kv_append_mla.argtypes = [ctypes.POINTER(MLADesc), vp, vp, vp, vp, vp]
+    lib.decode_kv_append_mla.restype = ctypes.c_int
     lib.paged_kv_gather.restype = ctypes.c_int
     lib.decode_attn_default_workers.argtypes = [ctypes.POINTER(PagedDesc), ctypes.POINTER(MLADesc),
                                                 ctypes.POINTER(i32)]
@@ -205,6 +210,42 @@ def paged_kv_gather(kv_pages: torch.Tensor, page_table: torch.Tensor, seq_lens: 
     return dense
 
 
+def decode_kv_append(k_new: torch.Tensor, v_new: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor,
+                     positions: torch.Tensor, *, k_scale: Optional[torch.Tensor] = None,
+                     v_scale: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Write each request's new K/V ([B][Hkv][D], fp32 or bf16) at token positions[b]
+    of its paged history in kv_pages [num_pages][2][Hkv][16][D] (fp32, bf16, or fp8
+    with k_scale/v_scale [Hkv]); a negative position skips the request.  In place;
+    returns kv_pages."""
+    _need_cuda(k_new, v_new, kv_pages, page_table, positions, k_scale, v_scale)
+    B, Hkv, D = k_new.shape
+    num_pages, two, Hkv2, P, D2 = kv_pages.shape
+    if two != 2 or Hkv2 != Hkv or D2 != D or tuple(v_new.shape) != (B, Hkv, D):
+        raise ValueError("k_new, v_new must be [B][Hkv][D] matching kv_pages [num_pages][2][Hkv][P][D]")
+    d = PagedDesc(B, Hkv, Hkv, D, P, num_pages, page_table.shape[1], dtype_tag(k_new), dtype_tag(kv_pages), 0,
+                  _ptr(k_scale), _ptr(v_scale))
+    st = _lib.decode_kv_append(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(kv_pages), _ptr(page_table),
+                               _ptr(positions), _stream(stream))
+    _check(st, "decode_kv_append")
+    return kv_pages
+
+
+def decode_kv_append_mla(latent_new: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor,
+                         positions: torch.Tensor, stream=None) -> torch.Tensor:
+    """Write each request's new bf16 latent ([B][576]) at token positions[b] of its
+    paged history in kv_pages [num_pages][P][576]; in place; returns kv_pages."""
+    _need_cuda(latent_new, kv_pages, page_table, positions)
+    B, Dk = latent_new.shape
+    num_pages, P, Dk2 = kv_pages.shape
+    if Dk2 != Dk:
+        raise ValueError("latent_new [B][576] must match kv_pages [num_pages][P][576]")
+    d = MLADesc(B, 128, Dk, 512, P, num_pages, page_table.shape[1], 0)
+    st = _lib.decode_kv_append_mla(ctypes.byref(d), _ptr(latent_new), _ptr(kv_pages), _ptr(page_table),
+                                   _ptr(positions), _stream(stream))
+    _check(st, "decode_kv_append_mla")
+    return kv_pages
+
+
 def default_workers(q: torch.Tensor = None, kv_pages: torch.Tensor = None, page_table: torch.Tensor = None,
                     *, mla_desc: Optional[MLADesc] = None, k_scale=None, v_scale=None) -> int:
     out = ctypes.c_int32(0)
@@ -231,4 +272,4 @@ def timer_end():
 
 
 __all__ = ["timer_begin", "timer_end", "decode_attn_paged", "decode_attn_mla", "decode_attn_plan", "paged_kv_gather", "default_workers",
-           "PagedDesc", "MLADesc", "DecodeAttnError", "LIB_PATH", "EXPORTS", "lib"]
+           "PagedDesc", "MLADesc", "DecodeAttnError", "LIB_PATH", "EXPORTS", "lib", "decode_kv_append", "decode_kv_append_mla"]

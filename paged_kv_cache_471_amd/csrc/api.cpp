@@ -12,7 +12,7 @@
 #include <vector>
 
 #include "../../include/decode_attn.h"
-#include "da_launch.h"
+#include "da_append.h"
 
 namespace {
 
@@ -413,6 +413,59 @@ int decode_attn_mla(const da_mla_desc* d, const void* q, const void* kv_pages, c
     e = da::launch_merge(mg, d->batch, s);
     if (e != hipSuccess) return hip_fail(e);
     return DA_OK;
+}
+
+int decode_kv_append(const da_paged_desc* d, const void* k_new, const void* v_new, void* kv_pages,
+                     const int32_t* page_table, const int32_t* positions, void* stream) {
+    int st = check_paged(d);
+    if (st != DA_OK) return st;
+    if (k_new == nullptr || v_new == nullptr || kv_pages == nullptr || page_table == nullptr || positions == nullptr)
+        return DA_ERR_NULL;
+    const size_t in_align = d->q_dtype == DA_F32 ? 16 : 8;
+    if (!aligned(k_new, in_align) || !aligned(v_new, in_align) || !aligned(kv_pages, 16) ||
+        !aligned(page_table, 4) || !aligned(positions, 4))
+        return DA_ERR_SHAPE;
+    if (d->batch == 0) return DA_OK;
+    da::AppendArgs a{};
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.kv = kv_pages;
+    a.page_table = page_table;
+    a.positions = positions;
+    a.k_scale = d->k_scale;
+    a.v_scale = d->v_scale;
+    a.batch = d->batch;
+    a.kv_heads = d->num_kv_heads;
+    a.head_dim = d->head_dim;
+    a.page_size = d->page_size;
+    a.max_pages = d->max_pages_per_seq;
+    a.in_dtype = d->q_dtype;
+    a.kv_dtype = d->kv_dtype;
+    hipError_t e = da::launch_kv_append(a, static_cast<hipStream_t>(stream), next_kernel_events());
+    return e == hipSuccess ? DA_OK : hip_fail(e);
+}
+
+int decode_kv_append_mla(const da_mla_desc* d, const void* latent_new, void* kv_pages, const int32_t* page_table,
+                         const int32_t* positions, void* stream) {
+    int st = check_mla(d);
+    if (st != DA_OK) return st;
+    if (latent_new == nullptr || kv_pages == nullptr || page_table == nullptr || positions == nullptr)
+        return DA_ERR_NULL;
+    if (!aligned(latent_new, 16) || !aligned(kv_pages, 16) || !aligned(page_table, 4) || !aligned(positions, 4))
+        return DA_ERR_SHAPE;
+    if (d->batch == 0) return DA_OK;
+    da::AppendArgs a{};
+    a.k_new = latent_new;
+    a.kv = kv_pages;
+    a.page_table = page_table;
+    a.positions = positions;
+    a.batch = d->batch;
+    a.page_size = d->page_size;
+    a.max_pages = d->max_pages_per_seq;
+    a.in_dtype = DA_BF16;
+    a.kv_dtype = DA_BF16;
+    hipError_t e = da::launch_kv_append_mla(a, static_cast<hipStream_t>(stream), next_kernel_events());
+    return e == hipSuccess ? DA_OK : hip_fail(e);
 }
 
 int decode_attn_plan(int32_t batch, const int32_t* seq_lens, int32_t page_size, int32_t units, int32_t workers,

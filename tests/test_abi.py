@@ -25,7 +25,8 @@ def lib():
 
 def test_header_declares_expected_entry_points():
     names = _declared()
-    for n in ("decode_attn_paged", "decode_attn_mla", "decode_attn_plan", "paged_kv_gather"):
+    for n in ("decode_attn_paged", "decode_attn_mla", "decode_attn_plan", "paged_kv_gather",
+              "decode_kv_append", "decode_kv_append_mla"):
         assert n in names
 
 
@@ -118,3 +119,35 @@ def test_mla_misaligned_rejected(lib):
     d = _mla_desc(lib)
     st = lib.lib().decode_attn_mla(ctypes.byref(d), FAKE + 8, FAKE, FAKE, FAKE, 0.05, FAKE, FAKE, None)
     assert st == -2
+
+
+# ---- KV append: the same descriptor checks, and its own pointer / alignment checks
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), -4),
+    (dict(q_dtype=0, kv_dtype=2), -3),                # fp32 into fp8: not offered
+    (dict(q_dtype=1, kv_dtype=2), -1),                # fp8 without scales
+    (dict(batch=-1), -2),
+])
+def test_append_invalid_descriptors_rejected(lib, kw, status):
+    d = _desc(lib, **kw)
+    st = lib.lib().decode_kv_append(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == status, lib.lib().decode_attn_status_str(st)
+
+
+def test_append_null_and_misaligned_rejected(lib):
+    d = _desc(lib)
+    L = lib.lib()
+    for i in range(5):
+        args = [FAKE] * 5
+        args[i] = None
+        assert L.decode_kv_append(ctypes.byref(d), *args, None) == -1
+    # fp32 new values must be 16-byte aligned
+    assert L.decode_kv_append(ctypes.byref(d), FAKE + 8, FAKE, FAKE, FAKE, FAKE, None) == -2
+    md = lib.MLADesc(batch=2, num_heads=128, latent_dim=576, v_dim=512, page_size=64, num_pages=8,
+                     max_pages_per_seq=4, workers=0)
+    assert L.decode_kv_append_mla(ctypes.byref(md), None, FAKE, FAKE, FAKE, None) == -1
+    assert L.decode_kv_append_mla(ctypes.byref(md), FAKE + 8, FAKE, FAKE, FAKE, None) == -2
+    md.latent_dim = 512
+    assert L.decode_kv_append_mla(ctypes.byref(md), FAKE, FAKE, FAKE, FAKE, None) < 0
