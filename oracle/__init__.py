@@ -22,19 +22,25 @@ What it follows (page titles of the source material):
   Fig. 1).
 * FP8 E4M3 KV carries scales (SPLASH, App. C.1 and App. B.1).
 
+* A request's query rows in a step: one in decode, the chunk length in
+  prefill; multi-token prediction of depth 1 gives two (OpWeave, §4.2;
+  Analytical Provisioning, App. B.1).
+
 Readings taken where the pages are silent are listed in the module docstrings
-of ``attention.py``, ``plan.py`` and ``append.py`` (the KV append that
-precedes each step).
+of ``attention.py``, ``plan.py``, ``append.py`` (the KV append that precedes
+each step) and ``rows.py`` (several query rows per request).
 """
 from .formats import bf16_bits_to_f64, fp8_e4m3fn_to_f64, fp8_e4m3fn_table, decode_storage
 from .attention import (gather_history, paged_decode_attention, mla_decode_attention,
                         attention_over_range, lse_merge, dense_attention)
 from .plan import partition, Partition
 from .append import fp8_e4m3fn_encode, kv_append, mla_kv_append
+from .rows import paged_decode_attention_rows, visible_tokens
 
 __all__ = [
     "bf16_bits_to_f64", "fp8_e4m3fn_to_f64", "fp8_e4m3fn_table", "decode_storage",
     "gather_history", "paged_decode_attention", "mla_decode_attention",
     "attention_over_range", "lse_merge", "dense_attention", "partition", "Partition",
     "fp8_e4m3fn_encode", "kv_append", "mla_kv_append",
+    "paged_decode_attention_rows", "visible_tokens",
 ]
