@@ -234,6 +234,42 @@ def time_append(attn, steps, warmup, step_ms):
             "kernel_pct_of_attention_step": round(100 * kms / step_ms, 2) if kms else None}
 
 
+class RowsRunner(GqaRunner):
+    """A GQA workload with several query rows per request (multi-token
+    prediction): the same histories, q and out [B][rows][Hq][D]."""
+
+    def __init__(self, cfg, rows, sets=2):
+        import numpy as np
+        import workloads as wl
+        from workloads import accounting
+        super().__init__(cfg, sets)
+        self.rows = rows
+        c = self.case
+        rng = np.random.default_rng(wl.BASE_SEED + rows)
+        q32 = rng.standard_normal((len(c.seq_lens), rows, cfg.q_heads, cfg.head_dim)).astype(np.float32)
+        self.q = _to_dev(q32 if cfg.q_dtype == wl.F32 else wl.to_bf16_bits(q32), cfg.q_dtype, "cuda")
+        self.out = self.q.new_empty(self.q.shape)
+        self.lse = self.lse.new_empty((len(c.seq_lens), rows, cfg.q_heads))
+        self.bytes = accounting.gqa_bytes(c.seq_lens, cfg.page_size, cfg.q_heads, cfg.kv_heads, cfg.head_dim,
+                                          cfg.q_dtype, cfg.kv_dtype, rows)
+        self.flops = accounting.gqa_flops(c.seq_lens, cfg.q_heads, cfg.head_dim, rows)
+
+    def step(self):
+        import paged_kv_cache_471_amd as da
+        kv = self.kvs[self.i % len(self.kvs)]
+        self.i += 1
+        da.decode_attn_paged_rows(self.q, kv, self.pt, self.sl, self.case.scale, self.out, self.lse,
+                                  k_scale=self.ks, v_scale=self.vs)
+
+    @property
+    def batch(self):
+        return self.rows * len(self.case.seq_lens)       # tokens decoded per step
+
+
+# secondary workloads with several query rows per request: name -> (workload, rows)
+ROWS_WORKLOADS = {"llama8b-mtp2": ("llama8b", 2)}
+
+
 def make_runner(cfg):
     import workloads as wl
     return MlaRunner(cfg) if isinstance(cfg, wl.MLAConfig) else GqaRunner(cfg)
@@ -318,7 +354,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b")
-    ap.add_argument("--secondary", default="skewed,mla,longfp8",
+    ap.add_argument("--secondary", default="skewed,mla,longfp8,llama8b-mtp2",
                     help="comma list of other workloads to report beside the headline ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -343,8 +379,13 @@ def main():
         copy_probe(args.copy_mb, args.steps)
         return
 
-    cfg = wl.CONFIGS[args.workload]
-    runner = make_runner(cfg)
+    if args.workload in ROWS_WORKLOADS:
+        base_name, rows = ROWS_WORKLOADS[args.workload]
+        cfg = wl.CONFIGS[base_name]
+        runner = RowsRunner(cfg, rows)
+    else:
+        cfg = wl.CONFIGS[args.workload]
+        runner = make_runner(cfg)
     print(f"# headline {cfg.name}: inputs generated in {runner.gen_s:.1f}s, "
           f"sum L = {runner.tokens}, {runner.bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
     if args.mode == "step":
@@ -396,15 +437,21 @@ def main():
 
     secondary = {}
     for name in [s for s in args.secondary.split(",") if s]:
-        scfg = wl.CONFIGS[name]
+        rows = 1
+        if name in ROWS_WORKLOADS:
+            base_name, rows = ROWS_WORKLOADS[name]
+            scfg = wl.CONFIGS[base_name]
+        else:
+            scfg = wl.CONFIGS[name]
         del runner
         torch.cuda.empty_cache()
-        runner2 = make_runner(scfg)
+        runner2 = RowsRunner(scfg, rows) if rows > 1 else make_runner(scfg)
         print(f"# secondary {name}: sum L = {runner2.tokens}, {runner2.bytes / 1e6:.1f} MB", file=sys.stderr,
               flush=True)
         sms, skms, _ = time_runner(runner2, max(10, args.steps // 2), max(3, args.warmup // 2), warm_s=SETTLE_S)
         sg = runner2.bytes / (sms * 1e-3) / 1e9
-        entry = {"workload": workload_desc(scfg), "ms_per_step": sms, "GBps": round(sg, 2),
+        desc = workload_desc(scfg) + (f", {rows} query rows per request (MTP depth {rows - 1})" if rows > 1 else "")
+        entry = {"workload": desc, "ms_per_step": sms, "GBps": round(sg, 2),
                  "pct_hbm_peak": round(100 * sg / HBM_PEAK_GBS, 2),
                  "kernel_ms": skms,
                  "kernel_GBps": round(runner2.bytes / (skms * 1e-3) / 1e9, 2) if skms else None,

@@ -149,6 +149,28 @@ int decode_attn_paged(const da_paged_desc* desc, const void* q, const void* kv_p
                       void* out, float* lse, void* stream);
 
 /*
+ * decode_attn_paged_rows - decode_attn_paged with q_rows query rows per
+ * request: a request's query rows in a step are one in plain decode and more
+ * with multi-token prediction (MTP depth 1 gives 2) or a short prefill chunk
+ * ("OpWeave", §4.2 Transition-aware scheduling, the rows q_i of each request;
+ * "Analytical Provisioning", App. B.1).  The rows are the last q_rows tokens
+ * of each history, already appended: row i sees positions
+ * t <= seq_lens[b] - q_rows + i (causal among the new rows, older history
+ * whole).  A row that sees no position (seq_lens[b] < q_rows - i) gets
+ * out = 0 and lse = -inf.
+ *   q_rows      1 .. 8, and q_rows * (Hq / Hkv) <= 8 (the kernels' largest
+ *               head group); DA_ERR_UNSUPPORTED beyond.
+ *   q           device, [B][q_rows][Hq][D] q_dtype.
+ *   out         device, [B][q_rows][Hq][D] q_dtype (written).
+ *   lse         device, fp32 [B][q_rows][Hq] (written), or NULL.
+ * Other arguments, layouts and errors as decode_attn_paged; each K/V page is
+ * read once for all rows.
+ */
+int decode_attn_paged_rows(const da_paged_desc* desc, int32_t q_rows, const void* q, const void* kv_pages,
+                           const int32_t* page_table, const int32_t* seq_lens, float scale,
+                           void* out, float* lse, void* stream);
+
+/*
  * decode_attn_mla - one decode step of absorbed MLA attention over the
  * head-shared latent.  Arguments as decode_attn_paged with the MLA layouts.
  */

@@ -21,7 +21,7 @@ DA_F32, DA_BF16, DA_FP8_E4M3 = 0, 1, 2
 STATUS = {0: "DA_OK", -1: "DA_ERR_NULL", -2: "DA_ERR_SHAPE", -3: "DA_ERR_DTYPE", -4: "DA_ERR_UNSUPPORTED",
           -5: "DA_ERR_WORKSPACE", -6: "DA_ERR_HIP"}
 
-EXPORTS = ("decode_attn_paged", "decode_attn_mla", "decode_attn_plan", "paged_kv_gather",
+EXPORTS = ("decode_attn_paged", "decode_attn_paged_rows", "decode_attn_mla", "decode_attn_plan", "paged_kv_gather",
            "decode_kv_append", "decode_kv_append_mla",
            "decode_attn_default_workers", "decode_attn_status_str", "decode_attn_last_hip_error",
            "decode_attn_timer_begin", "decode_attn_timer_end")
@@ -57,6 +57,8 @@ def _load():
     vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
     lib.decode_attn_paged.argtypes = [ctypes.POINTER(PagedDesc), vp, vp, vp, vp, f32, vp, vp, vp]
     lib.decode_attn_paged.restype = ctypes.c_int
+    lib.decode_attn_paged_rows.argtypes = [ctypes.POINTER(PagedDesc), i32, vp, vp, vp, vp, f32, vp, vp, vp]
+    lib.decode_attn_paged_rows.restype = ctypes.c_int
     lib.decode_attn_mla.argtypes = [ctypes.POINTER(MLADesc), vp, vp, vp, vp, f32, vp, vp, vp]
     lib.decode_attn_mla.restype = ctypes.c_int
     lib.decode_attn_plan.argtypes = [i32, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
@@ -152,6 +154,31 @@ def decode_attn_paged(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch
     st = _lib.decode_attn_paged(ctypes.byref(d), _ptr(q), _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens),
                                 float(scale), _ptr(out), _ptr(lse), _stream(stream))
     _check(st, "decode_attn_paged")
+    return out, lse
+
+
+def decode_attn_paged_rows(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor,
+                           seq_lens: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
+                           lse: Optional[torch.Tensor] = None, *, k_scale: Optional[torch.Tensor] = None,
+                           v_scale: Optional[torch.Tensor] = None, workers: int = 0, want_lse: bool = True,
+                           stream=None):
+    """Paged GQA decode attention with several query rows per request.  q
+    [B][n][Hq][D]: row i of request b is the token at position seq_lens[b] - n + i
+    and sees positions up to its own.  Returns (out [B][n][Hq][D] in q's dtype,
+    lse [B][n][Hq] fp32 or None)."""
+    _need_cuda(q, kv_pages, page_table, seq_lens, k_scale, v_scale)
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B][rows][Hq][D], got {tuple(q.shape)}")
+    B, n, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, n, Hq), dtype=torch.float32, device=q.device)
+    _need_cuda(out, lse)
+    d = paged_desc(q[:, 0], kv_pages, page_table, k_scale=k_scale, v_scale=v_scale, workers=workers)
+    st = _lib.decode_attn_paged_rows(ctypes.byref(d), n, _ptr(q), _ptr(kv_pages), _ptr(page_table),
+                                     _ptr(seq_lens), float(scale), _ptr(out), _ptr(lse), _stream(stream))
+    _check(st, "decode_attn_paged_rows")
     return out, lse
 
 
@@ -271,5 +298,5 @@ def timer_end():
     return ms.value, n.value
 
 
-__all__ = ["timer_begin", "timer_end", "decode_attn_paged", "decode_attn_mla", "decode_attn_plan", "paged_kv_gather", "default_workers",
+__all__ = ["timer_begin", "timer_end", "decode_attn_paged", "decode_attn_paged_rows", "decode_attn_mla", "decode_attn_plan", "paged_kv_gather", "default_workers",
            "PagedDesc", "MLADesc", "DecodeAttnError", "LIB_PATH", "EXPORTS", "lib", "decode_kv_append", "decode_kv_append_mla"]

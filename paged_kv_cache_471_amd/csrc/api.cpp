@@ -182,7 +182,17 @@ int check_paged(const da_paged_desc* d) {
     return DA_OK;
 }
 
-int resolve_gqa_workers(const da_paged_desc* d, int* G) {
+// (row, head) members of one KV head's group in the GQA kernel: q_rows times
+// the query heads per KV head, padded to a power of two; 0 when no kernel has
+// that many.
+int gqa_members(const da_paged_desc* d, int q_rows) {
+    const int want = q_rows * (d->num_q_heads / d->num_kv_heads);
+    int gs = 1;
+    while (gs < want) gs <<= 1;
+    return gs <= 8 ? gs : 0;
+}
+
+int resolve_gqa_workers(const da_paged_desc* d, int members, int* G) {
     if (d->workers > 0) {
         *G = d->workers;
         return DA_OK;
@@ -190,10 +200,10 @@ int resolve_gqa_workers(const da_paged_desc* d, int* G) {
     int cus = 0;
     int st = device_cus(&cus);
     if (st != DA_OK) return st;
-    const int group = d->num_q_heads / d->num_kv_heads;
-    const int waves = da::gqa_waves_per_cu(d->q_dtype, d->kv_dtype, d->head_dim, group);
-    if (waves <= 0) return DA_ERR_UNSUPPORTED;
-    int g = cus * waves;
+    const int group_log2 = __builtin_ctz(static_cast<unsigned>(d->num_q_heads / d->num_kv_heads));
+    const int per_cu = da::gqa_workers_per_cu(d->q_dtype, d->kv_dtype, d->head_dim, members, group_log2);
+    if (per_cu <= 0) return DA_ERR_UNSUPPORTED;
+    int g = cus * per_cu;
     if (g > da::kMaxWorkers) g = da::kMaxWorkers;
     *G = g;
     return DA_OK;
@@ -226,6 +236,84 @@ int resolve_mla_workers(const da_mla_desc* d, int* G) {
     if (g <= 0) return DA_ERR_UNSUPPORTED;
     if (g > da::kMlaMaxWorkers) g = da::kMlaMaxWorkers;
     *G = g;
+    return DA_OK;
+}
+
+int gqa_step(const da_paged_desc* d, int q_rows, const void* q, const void* kv_pages, const int32_t* page_table,
+             const int32_t* seq_lens, float scale, void* out, float* lse, void* stream) {
+    int st = check_paged(d);
+    if (st != DA_OK) return st;
+    if (q_rows < 1 || q_rows > 8) return q_rows < 1 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
+    const int members = gqa_members(d, q_rows);
+    if (members == 0) return DA_ERR_UNSUPPORTED;
+    if (q == nullptr || kv_pages == nullptr || page_table == nullptr || seq_lens == nullptr || out == nullptr)
+        return DA_ERR_NULL;
+    const int elem_kv = d->kv_dtype == DA_F32 ? 4 : (d->kv_dtype == DA_BF16 ? 2 : 1);
+    const size_t lane_bytes = static_cast<size_t>(d->head_dim / 16) * elem_kv;
+    if (!aligned(kv_pages, lane_bytes < 16 ? lane_bytes : 16) || !aligned(q, 16) || !aligned(out, 16) ||
+        !aligned(lse, 4) || !aligned(page_table, 4) || !aligned(seq_lens, 4))
+        return DA_ERR_SHAPE;
+    if (!(scale == scale)) return DA_ERR_SHAPE;
+    if (d->batch == 0) return DA_OK;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int G = 0;
+    st = resolve_gqa_workers(d, members, &G);
+    if (st != DA_OK) return st;
+    const int group = d->num_q_heads / d->num_kv_heads;
+    const int group_log2 = __builtin_ctz(static_cast<unsigned>(group));
+    const int streams = d->batch * d->num_kv_heads;
+    SplitBuffers sb;
+    st = get_split_buffers(s, streams, G, members, d->head_dim, &sb);
+    if (st != DA_OK) return st;
+
+    da::GqaArgs ga{};
+    ga.q = q;
+    ga.kv = kv_pages;
+    ga.page_table = page_table;
+    ga.seq_lens = seq_lens;
+    ga.k_scale = d->k_scale;
+    ga.v_scale = d->v_scale;
+    ga.scale_log2 = scale * 1.4426950408889634f;
+    ga.batch = d->batch;
+    ga.q_heads = d->num_q_heads;
+    ga.kv_heads = d->num_kv_heads;
+    ga.page_size = d->page_size;
+    ga.max_pages = d->max_pages_per_seq;
+    ga.workers = G;
+    ga.q_rows = q_rows;
+    ga.group_log2 = group_log2;
+    ga.plan_info = sb.plan_info;
+    ga.stream_info = sb.stream_info;
+    ga.out = out;
+    ga.lse = lse;
+    ga.o_part = sb.o_part;
+    ga.lse_part = sb.lse_part;
+    hipError_t e = da::launch_gqa(d->q_dtype, d->kv_dtype, d->head_dim, members, ga, s, next_kernel_events());
+    if (e != hipSuccess) return hip_fail(e);
+
+    da::MergeArgs ma{};
+    ma.seq_lens = seq_lens;
+    ma.plan_info = sb.plan_info;
+    ma.stream_info = sb.stream_info;
+    ma.o_part = sb.o_part;
+    ma.lse_part = sb.lse_part;
+    ma.out = out;
+    ma.lse = lse;
+    ma.units = d->num_kv_heads;
+    ma.group = members;
+    ma.dim = d->head_dim;
+    ma.rows = q_rows;
+    ma.group_log2 = group_log2;
+    // Streams split into about two pieces or fewer are merged by one
+    // workgroup for all the heads of their group (fewer, fuller workgroups;
+    // most of them return at once); more deeply split streams by one
+    // workgroup per head, so that their pieces spread over more lanes.
+    const int pieces = ga.workers / (streams > 0 ? streams : 1);
+    ma.heads_per_block = pieces <= 2 && members * d->head_dim <= 4 * 256 ? members : 1;
+    ma.out_is_bf16 = d->q_dtype == DA_BF16;
+    e = da::launch_merge(ma, streams, s);
+    if (e != hipSuccess) return hip_fail(e);
     return DA_OK;
 }
 
@@ -289,72 +377,13 @@ int decode_attn_timer_end(double* total_ms, int32_t* launches) {
 
 int decode_attn_paged(const da_paged_desc* d, const void* q, const void* kv_pages, const int32_t* page_table,
                       const int32_t* seq_lens, float scale, void* out, float* lse, void* stream) {
-    int st = check_paged(d);
-    if (st != DA_OK) return st;
-    if (q == nullptr || kv_pages == nullptr || page_table == nullptr || seq_lens == nullptr || out == nullptr)
-        return DA_ERR_NULL;
-    const int elem_kv = d->kv_dtype == DA_F32 ? 4 : (d->kv_dtype == DA_BF16 ? 2 : 1);
-    const size_t lane_bytes = static_cast<size_t>(d->head_dim / 16) * elem_kv;
-    if (!aligned(kv_pages, lane_bytes < 16 ? lane_bytes : 16) || !aligned(q, 16) || !aligned(out, 16) ||
-        !aligned(lse, 4) || !aligned(page_table, 4) || !aligned(seq_lens, 4))
-        return DA_ERR_SHAPE;
-    if (!(scale == scale)) return DA_ERR_SHAPE;
-    if (d->batch == 0) return DA_OK;
+    return gqa_step(d, 1, q, kv_pages, page_table, seq_lens, scale, out, lse, stream);
+}
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    int G = 0;
-    st = resolve_gqa_workers(d, &G);
-    if (st != DA_OK) return st;
-    const int group = d->num_q_heads / d->num_kv_heads;
-    const int streams = d->batch * d->num_kv_heads;
-    SplitBuffers sb;
-    st = get_split_buffers(s, streams, G, group, d->head_dim, &sb);
-    if (st != DA_OK) return st;
-
-    da::GqaArgs ga{};
-    ga.q = q;
-    ga.kv = kv_pages;
-    ga.page_table = page_table;
-    ga.seq_lens = seq_lens;
-    ga.k_scale = d->k_scale;
-    ga.v_scale = d->v_scale;
-    ga.scale_log2 = scale * 1.4426950408889634f;
-    ga.batch = d->batch;
-    ga.q_heads = d->num_q_heads;
-    ga.kv_heads = d->num_kv_heads;
-    ga.page_size = d->page_size;
-    ga.max_pages = d->max_pages_per_seq;
-    ga.workers = G;
-    ga.plan_info = sb.plan_info;
-    ga.stream_info = sb.stream_info;
-    ga.out = out;
-    ga.lse = lse;
-    ga.o_part = sb.o_part;
-    ga.lse_part = sb.lse_part;
-    hipError_t e = da::launch_gqa(d->q_dtype, d->kv_dtype, d->head_dim, group, ga, s, next_kernel_events());
-    if (e != hipSuccess) return hip_fail(e);
-
-    da::MergeArgs ma{};
-    ma.seq_lens = seq_lens;
-    ma.plan_info = sb.plan_info;
-    ma.stream_info = sb.stream_info;
-    ma.o_part = sb.o_part;
-    ma.lse_part = sb.lse_part;
-    ma.out = out;
-    ma.lse = lse;
-    ma.units = d->num_kv_heads;
-    ma.group = group;
-    ma.dim = d->head_dim;
-    // Streams split into about two pieces or fewer are merged by one
-    // workgroup for all the heads of their group (fewer, fuller workgroups;
-    // most of them return at once); more deeply split streams by one
-    // workgroup per head, so that their pieces spread over more lanes.
-    const int pieces = ga.workers / (streams > 0 ? streams : 1);
-    ma.heads_per_block = pieces <= 2 && group * d->head_dim <= 4 * 256 ? group : 1;
-    ma.out_is_bf16 = d->q_dtype == DA_BF16;
-    e = da::launch_merge(ma, streams, s);
-    if (e != hipSuccess) return hip_fail(e);
-    return DA_OK;
+int decode_attn_paged_rows(const da_paged_desc* d, int32_t q_rows, const void* q, const void* kv_pages,
+                           const int32_t* page_table, const int32_t* seq_lens, float scale, void* out, float* lse,
+                           void* stream) {
+    return gqa_step(d, q_rows, q, kv_pages, page_table, seq_lens, scale, out, lse, stream);
 }
 
 int decode_attn_mla(const da_mla_desc* d, const void* q, const void* kv_pages, const int32_t* page_table,
@@ -408,6 +437,8 @@ int decode_attn_mla(const da_mla_desc* d, const void* q, const void* kv_pages, c
     mg.units = 1;
     mg.group = d->num_heads;
     mg.dim = d->v_dim;
+    mg.rows = 1;
+    mg.group_log2 = __builtin_ctz(static_cast<unsigned>(d->num_heads));
     mg.heads_per_block = d->num_heads >= 8 ? 8 : d->num_heads;
     mg.out_is_bf16 = 1;
     e = da::launch_merge(mg, d->batch, s);
@@ -532,7 +563,7 @@ int decode_attn_default_workers(const da_paged_desc* gqa, const da_mla_desc* mla
         if (st != DA_OK) return st;
         da_paged_desc dd = *gqa;
         dd.workers = 0;
-        st = resolve_gqa_workers(&dd, &G);
+        st = resolve_gqa_workers(&dd, gqa_members(&dd, 1), &G);
     } else {
         st = check_mla(mla);
         if (st != DA_OK) return st;

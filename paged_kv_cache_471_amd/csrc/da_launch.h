@@ -31,12 +31,18 @@ struct GqaArgs {
     const float* v_scale;
     float scale_log2;       // softmax scale * log2(e)
     int batch, q_heads, kv_heads, page_size, max_pages, workers;
+    // Query rows per request (q, out [batch][q_rows][q_heads][head_dim]): row i
+    // sees history positions t <= len - q_rows + i.  The kernel's head group
+    // GS holds the q_rows x (q_heads / kv_heads) (row, head) pairs of one KV
+    // head, row-major, padded to a power of two; group_log2 = log2 of the
+    // query heads per KV head.
+    int q_rows, group_log2;
     int2* plan_info;        // [1]: (W, active workers), written by worker 0
     int2* stream_info;      // [batch * kv_heads]: (first unit, pieces) of each non-empty stream
     void* out;
-    float* lse;
-    float* o_part;          // [2 * workers][group][head_dim]
-    float* lse_part;        // [2 * workers][group]   (log2 domain)
+    float* lse;             // [batch][q_rows][q_heads] or null
+    float* o_part;          // [2 * workers][GS][head_dim]
+    float* lse_part;        // [2 * workers][GS]   (log2 domain)
 };
 
 // Absorbed MLA: one head-shared latent of kMlaLatent bf16 values per token;
@@ -74,13 +80,15 @@ struct MergeArgs {
     const int2* stream_info;
     const float* o_part;    // [2 * workers][group][dim]
     const float* lse_part;  // [2 * workers][group]  (log2 domain)
-    void* out;              // [batch][units * group][dim], bf16 or fp32
-    float* lse;             // [batch][units * group] or null
+    void* out;              // [batch][rows][units << group_log2][dim], bf16 or fp32
+    float* lse;             // [batch][rows][units << group_log2] or null
     int units;              // streams per request (KV heads, or 1 for MLA)
-    int group;              // heads per stream
+    int group;              // (row, head) slots per stream in the partials
     int dim;                // values per head
     int heads_per_block;    // divides group
     int out_is_bf16;
+    int rows;               // query rows per request; slot h is row h >> group_log2
+    int group_log2;         // log2 of the query heads per stream
 };
 
 struct GatherArgs {
@@ -111,10 +119,13 @@ bool mla_heads_supported(int heads);
 int mla_blocks_per_worker(int heads);
 
 // Returns hipErrorInvalidValue if no kernel exists for this combination.
-hipError_t launch_gqa(int q_dtype, int kv_dtype, int head_dim, int group, const GqaArgs& a, hipStream_t s,
+// members: the kernel's head group (GqaArgs); a.group_log2 selects the
+// single-row (members == 2^group_log2) or multi-row variant.
+hipError_t launch_gqa(int q_dtype, int kv_dtype, int head_dim, int members, const GqaArgs& a, hipStream_t s,
                       const KernelEvents& ev);
-// Wavefronts of the GQA kernel that fit on one CU at once (0 if no kernel).
-int gqa_waves_per_cu(int q_dtype, int kv_dtype, int head_dim, int group);
+// Workers of the GQA kernel that fit on one CU at once (0 if no kernel); a
+// worker is one wavefront, or two for multi-row groups of 8 members.
+int gqa_workers_per_cu(int q_dtype, int kv_dtype, int head_dim, int members, int group_log2);
 constexpr int kGqaBlock = 256;   // 4 wavefronts per workgroup, each an independent worker
 
 }  // namespace da

@@ -31,6 +31,13 @@
 //    stream writes out/lse, otherwise (o, log2-sum-exp) goes to a partial slot
 //    that the merge kernel (merge.hip) combines.
 //  * Each wave plans its own share (da_plan.h): no planner launch precedes it.
+//  * Several query rows per request (multi-token prediction, short prefill
+//    chunks: "OpWeave", §4.2, a request's query rows in a step; "Analytical
+//    Provisioning", App. B.1, MTP depth 1) are the last q_rows tokens of the
+//    history; row i sees positions t <= len - q_rows + i.  The (row, head)
+//    pairs that share a KV head form the kernel's head group, so every K/V
+//    page is still read once per step; the causal limit differs between the
+//    group's members only on the last page or two.
 #include <hip/hip_ext.h>
 
 #include "da_common.h"
@@ -111,24 +118,38 @@ __device__ __forceinline__ void cursor_next(Cursor& c, const int32_t* seq_lens, 
     } while (c.pages == 0);
 }
 
-template <int QT, int KV, int D, int GS>
+// A KV head's group has MT = GS * SP (row, head) members; RG = log2 of the
+// query heads per KV head.  MT > 2^RG means several query rows per request
+// (their count is read from the arguments); MT == 2^RG is the single-row
+// step, where all row arithmetic folds away at compile time.  SP waves of one
+// workgroup form one worker: they walk the same share of units, each with GS
+// of the members, so each holds half the softmax state (two waves per SIMD
+// instead of one) while the second read of every page hits the cache.
+template <int QT, int KV, int D, int GS, int RG, int SP>
 __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
     using C = Cfg<QT, KV, D, GS>;
+    constexpr int MT = GS * SP;               // members of a KV head's group
+    constexpr bool MR = MT > (1 << RG);
     constexpr int DL = C::DL, NW = C::NW, QW = C::QW, EB = C::EB;
 
     const int lane = threadIdx.x & 63;
     const int row = lane >> 4;            // token row within a group of 4 tokens
     const int col = lane & 15;            // dim slice
-    const int g = uniform(blockIdx.x * (kGqaBlock / 64) + (threadIdx.x >> 6));
+    const int wid = uniform(blockIdx.x * (kGqaBlock / 64) + (threadIdx.x >> 6));
+    const int g = SP == 1 ? wid : wid / SP;   // worker
+    const int m_off = SP == 1 ? 0 : (wid % SP) * GS;   // first member of this wave
     if (g >= a.workers) return;
     const int Hkv = a.kv_heads;
     const int Hq = a.q_heads;
+    const int NR = MR ? a.q_rows : 1;         // query rows per request
+    constexpr int gl2 = RG;                   // log2(query heads per KV head)
+    const int gmask = (1 << gl2) - 1;
 
     const WaveShare sh = plan_share(a.seq_lens, a.batch, kPage, Hkv, a.workers, g);
-    if (sh.has_empty) {
+    if (sh.has_empty && m_off == 0) {
         // requests with no history: out = 0, lse = -inf
         for_each_empty_request(a.seq_lens, a.batch, a.workers, g, [&](int b) {
-            const int row_elems = Hq * D;
+            const int row_elems = NR * Hq * D;
             if constexpr (QT == kF32) {
                 float* o = static_cast<float*>(a.out) + static_cast<int64_t>(b) * row_elems;
                 for (int i = lane; i < row_elems; i += 64) o[i] = 0.0f;
@@ -137,11 +158,11 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
                 for (int i = lane; i < row_elems; i += 64) o[i] = 0;
             }
             if (a.lse != nullptr)
-                for (int h = lane; h < Hq; h += 64) a.lse[static_cast<int64_t>(b) * Hq + h] = -__builtin_inff();
+                for (int h = lane; h < NR * Hq; h += 64) a.lse[static_cast<int64_t>(b) * NR * Hq + h] = -__builtin_inff();
         });
     }
     const int NA = sh.active;             // active workers
-    if (g == 0 && lane == 0) *a.plan_info = make_int2(static_cast<int>(sh.W), NA);
+    if (g == 0 && lane == 0 && m_off == 0) *a.plan_info = make_int2(static_cast<int>(sh.W), NA);
     if (g >= NA) return;
     const int64_t c0 = sh.c0;
     const int n = static_cast<int>(sh.c1 - sh.c0);
@@ -171,13 +192,26 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
         for (int i = 0; i < kTPL; ++i) load_words<NW>(buf.v[i], vbase + i * 4 * D * EB);
     };
 
+    // This wave's member hh is member m = m_off + hh of the group: query row
+    // m >> gl2 of the request and query head (j << gl2) + (m & gmask); members
+    // past the last row pad the group and are neither loaded nor written.
+    auto row_of = [&](int hh) -> int { return (m_off + hh) >> gl2; };
+    auto q_index = [&](int b, int j, int hh) -> int64_t {
+        return (static_cast<int64_t>(b) * NR + row_of(hh)) * Hq + (j << gl2) + ((m_off + hh) & gmask);
+    };
+
     // query registers of the current stream's head group
     uint32_t qb[GS][QW];
     float qf[GS][QW];
     auto load_q = [&](int b, int j) {
 #pragma unroll
         for (int hh = 0; hh < GS; ++hh) {
-            const int64_t base = (static_cast<int64_t>(b) * Hq + j * GS + hh) * D + col * DL;
+            if (row_of(hh) >= NR) {
+#pragma unroll
+                for (int w = 0; w < QW; ++w) { qb[hh][w] = 0u; qf[hh][w] = 0.0f; }
+                continue;
+            }
+            const int64_t base = q_index(b, j, hh) * D + col * DL;
             if constexpr (C::kDot) {
                 const uint32_t* src = reinterpret_cast<const uint32_t*>(
                     static_cast<const uint16_t*>(a.q) + base);
@@ -216,7 +250,8 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
 
     auto process = [&](PageBuf<NW>& buf) {
         const int nvalid = cc.len - cc.p * kPage;   // >= 1
-        const bool tail = nvalid < kPage;
+        // the page holds a position that some row may not see
+        const bool tail = nvalid - (NR - 1) < kPage;
         float s[GS][kTPL];
 #pragma unroll
         for (int i = 0; i < kTPL; ++i) {
@@ -261,9 +296,11 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
         if (tail) {
 #pragma unroll
             for (int i = 0; i < kTPL; ++i) {
-                if (i * 4 + row >= nvalid) {
+                const int t = i * 4 + row;
 #pragma unroll
-                    for (int hh = 0; hh < GS; ++hh) s[hh][i] = -__builtin_inff();
+                for (int hh = 0; hh < GS; ++hh)
+                    if (t >= nvalid - (NR - 1) + row_of(hh)) s[hh][i] = -__builtin_inff();
+                if (t >= nvalid) {
 #pragma unroll
                     for (int w = 0; w < NW; ++w) buf.v[i].w[w] = 0u;
                 }
@@ -347,11 +384,15 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
         }
 #pragma unroll
         for (int hh = 0; hh < GS; ++hh) {
-            if ((hh & 3) != row) continue;
-            const float inv = vsc / l[hh];
-            const float lse2 = m[hh] + __builtin_log2f(l[hh]);
+            if ((hh & 3) != row || row_of(hh) >= NR) continue;
+            // a row that sees no position of this piece (only with several
+            // rows): o = 0, log-sum-exp -inf
+            const bool seen = l[hh] > 0.0f;
+            const float inv = seen ? vsc / l[hh] : 0.0f;
+            const float lse2 = seen ? m[hh] + __builtin_log2f(l[hh]) : -__builtin_inff();
             if (whole) {
-                const int64_t o = (static_cast<int64_t>(cc.b) * Hq + cc.j * GS + hh) * D + col * DL;
+                const int64_t qi = q_index(cc.b, cc.j, hh);
+                const int64_t o = qi * D + col * DL;
                 if constexpr (QT == kF32) {
                     float* dst = static_cast<float*>(a.out) + o;
 #pragma unroll
@@ -368,13 +409,12 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
 #pragma unroll
                     for (int d = 0; d < DL / 2; ++d) dst[d] = packed[d];
                 }
-                if (col == 0 && a.lse != nullptr)
-                    a.lse[static_cast<int64_t>(cc.b) * Hq + cc.j * GS + hh] = lse2 * kLn2;
+                if (col == 0 && a.lse != nullptr) a.lse[qi] = lse2 * kLn2;
             } else {
-                float* dst = a.o_part + (static_cast<int64_t>(slot) * GS + hh) * D + col * DL;
+                float* dst = a.o_part + (static_cast<int64_t>(slot) * MT + m_off + hh) * D + col * DL;
 #pragma unroll
                 for (int d = 0; d < DL; ++d) dst[d] = acc[hh][d] * inv;
-                if (col == 0) a.lse_part[static_cast<int64_t>(slot) * GS + hh] = lse2;
+                if (col == 0) a.lse_part[static_cast<int64_t>(slot) * MT + m_off + hh] = lse2;
             }
         }
     };
@@ -404,7 +444,7 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
     // The wave holding a stream's first piece records where the stream starts
     // and over how many workers it is split, for the merge kernel.
     auto record_stream = [&](int64_t start) {
-        if (lane != 0) return;
+        if (lane != 0 || m_off != 0) return;
         const int gf = first_worker_of(start, sh.W, NA);
         const int gl = last_worker_of(start + cc.pages, sh.W, NA);
         a.stream_info[cc.b * Hkv + cc.j] = make_int2(static_cast<int>(start), gl - gf + 1);
@@ -448,67 +488,89 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
     }
 }
 
-template <int QT, int KV, int D, int GS>
+template <int QT, int KV, int D, int GS, int RG, int SP>
 hipError_t launch_one(const GqaArgs& a, hipStream_t s, const KernelEvents& ev) {
     const int per_block = kGqaBlock / 64;
-    const int grid = (a.workers + per_block - 1) / per_block;
+    const int grid = (a.workers * SP + per_block - 1) / per_block;
     if (ev.start != nullptr)
-        hipExtLaunchKernelGGL((gqa_attn_kernel<QT, KV, D, GS>), dim3(grid), dim3(kGqaBlock), 0, s, ev.start,
-                              ev.stop, 0, a);
+        hipExtLaunchKernelGGL((gqa_attn_kernel<QT, KV, D, GS, RG, SP>), dim3(grid), dim3(kGqaBlock), 0, s,
+                              ev.start, ev.stop, 0, a);
     else
-        hipLaunchKernelGGL((gqa_attn_kernel<QT, KV, D, GS>), dim3(grid), dim3(kGqaBlock), 0, s, a);
+        hipLaunchKernelGGL((gqa_attn_kernel<QT, KV, D, GS, RG, SP>), dim3(grid), dim3(kGqaBlock), 0, s, a);
     return hipGetLastError();
 }
 
-template <int QT, int KV, int D, int GS>
-int waves_one() {
+// workers (SP waves each) of the variant that fit on one CU at once
+template <int QT, int KV, int D, int GS, int RG, int SP>
+int workers_one() {
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, gqa_attn_kernel<QT, KV, D, GS>, kGqaBlock, 0) !=
-        hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, gqa_attn_kernel<QT, KV, D, GS, RG, SP>, kGqaBlock,
+                                                     0) != hipSuccess)
         return 0;
-    return blocks * (kGqaBlock / 64);
+    return blocks * (kGqaBlock / 64) / SP;
 }
 
+// per_cu != null: report the workers per CU of the variant instead of launching it
+template <int QT, int KV, int D, int GS, int RG, int SP = 1>
+hipError_t run_or_size(const GqaArgs* a, hipStream_t s, const KernelEvents& ev, int* per_cu) {
+    if (per_cu != nullptr) {
+        *per_cu = workers_one<QT, KV, D, GS, RG, SP>();
+        return hipSuccess;
+    }
+    return launch_one<QT, KV, D, GS, RG, SP>(*a, s, ev);
+}
+
+// (members, log2 query heads per KV head): the single-row groups 1..8 and the
+// multi-row shapes that fit in 8 members; 8-member multi-row groups are split
+// over two waves of 4.
 template <int QT, int KV, int D>
-hipError_t by_group(int group, const GqaArgs* a, hipStream_t s, const KernelEvents& ev, int* waves) {
-    switch (group) {
-        case 1: if (waves) { *waves = waves_one<QT, KV, D, 1>(); return hipSuccess; } return launch_one<QT, KV, D, 1>(*a, s, ev);
-        case 2: if (waves) { *waves = waves_one<QT, KV, D, 2>(); return hipSuccess; } return launch_one<QT, KV, D, 2>(*a, s, ev);
-        case 4: if (waves) { *waves = waves_one<QT, KV, D, 4>(); return hipSuccess; } return launch_one<QT, KV, D, 4>(*a, s, ev);
-        case 8: if (waves) { *waves = waves_one<QT, KV, D, 8>(); return hipSuccess; } return launch_one<QT, KV, D, 8>(*a, s, ev);
+hipError_t by_group(int members, int rg, const GqaArgs* a, hipStream_t s, const KernelEvents& ev, int* per_cu) {
+    switch (members * 8 + rg) {
+        case 1 * 8 + 0: return run_or_size<QT, KV, D, 1, 0>(a, s, ev, per_cu);
+        case 2 * 8 + 1: return run_or_size<QT, KV, D, 2, 1>(a, s, ev, per_cu);
+        case 4 * 8 + 2: return run_or_size<QT, KV, D, 4, 2>(a, s, ev, per_cu);
+        case 8 * 8 + 3: return run_or_size<QT, KV, D, 8, 3>(a, s, ev, per_cu);
+        case 2 * 8 + 0: return run_or_size<QT, KV, D, 2, 0>(a, s, ev, per_cu);
+        case 4 * 8 + 0: return run_or_size<QT, KV, D, 4, 0>(a, s, ev, per_cu);
+        case 4 * 8 + 1: return run_or_size<QT, KV, D, 4, 1>(a, s, ev, per_cu);
+        case 8 * 8 + 0: return run_or_size<QT, KV, D, 4, 0, 2>(a, s, ev, per_cu);
+        case 8 * 8 + 1: return run_or_size<QT, KV, D, 4, 1, 2>(a, s, ev, per_cu);
+        case 8 * 8 + 2: return run_or_size<QT, KV, D, 4, 2, 2>(a, s, ev, per_cu);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <int QT, int KV>
-hipError_t by_dim(int dim, int group, const GqaArgs* a, hipStream_t s, const KernelEvents& ev, int* waves) {
+hipError_t by_dim(int dim, int members, int rg, const GqaArgs* a, hipStream_t s, const KernelEvents& ev,
+                  int* waves) {
     switch (dim) {
-        case 64: return by_group<QT, KV, 64>(group, a, s, ev, waves);
-        case 128: return by_group<QT, KV, 128>(group, a, s, ev, waves);
+        case 64: return by_group<QT, KV, 64>(members, rg, a, s, ev, waves);
+        case 128: return by_group<QT, KV, 128>(members, rg, a, s, ev, waves);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t dispatch(int q_dtype, int kv_dtype, int dim, int group, const GqaArgs* a, hipStream_t s,
+hipError_t dispatch(int q_dtype, int kv_dtype, int dim, int members, int rg, const GqaArgs* a, hipStream_t s,
                     const KernelEvents& ev, int* waves) {
-    if (q_dtype == kF32 && kv_dtype == kF32) return by_dim<kF32, kF32>(dim, group, a, s, ev, waves);
-    if (q_dtype == kBF16 && kv_dtype == kBF16) return by_dim<kBF16, kBF16>(dim, group, a, s, ev, waves);
-    if (q_dtype == kBF16 && kv_dtype == kFP8) return by_dim<kBF16, kFP8>(dim, group, a, s, ev, waves);
+    if (q_dtype == kF32 && kv_dtype == kF32) return by_dim<kF32, kF32>(dim, members, rg, a, s, ev, waves);
+    if (q_dtype == kBF16 && kv_dtype == kBF16) return by_dim<kBF16, kBF16>(dim, members, rg, a, s, ev, waves);
+    if (q_dtype == kBF16 && kv_dtype == kFP8) return by_dim<kBF16, kFP8>(dim, members, rg, a, s, ev, waves);
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_gqa(int q_dtype, int kv_dtype, int head_dim, int group, const GqaArgs& a, hipStream_t s,
+hipError_t launch_gqa(int q_dtype, int kv_dtype, int head_dim, int members, const GqaArgs& a, hipStream_t s,
                       const KernelEvents& ev) {
-    return dispatch(q_dtype, kv_dtype, head_dim, group, &a, s, ev, nullptr);
+    return dispatch(q_dtype, kv_dtype, head_dim, members, a.group_log2, &a, s, ev, nullptr);
 }
 
-int gqa_waves_per_cu(int q_dtype, int kv_dtype, int head_dim, int group) {
-    int waves = 0;
-    if (dispatch(q_dtype, kv_dtype, head_dim, group, nullptr, nullptr, KernelEvents{}, &waves) != hipSuccess)
+int gqa_workers_per_cu(int q_dtype, int kv_dtype, int head_dim, int members, int group_log2) {
+    int per_cu = 0;
+    if (dispatch(q_dtype, kv_dtype, head_dim, members, group_log2, nullptr, nullptr, KernelEvents{}, &per_cu) !=
+        hipSuccess)
         return 0;
-    return waves;
+    return per_cu;
 }
 
 }  // namespace da

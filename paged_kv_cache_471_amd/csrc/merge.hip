@@ -12,6 +12,12 @@
 // the whole GPU, so a stream split over many workers (a long request on few
 // streams) is merged with many loads in flight rather than by one worker.
 // Every reduction runs in a fixed order, so results are deterministic.
+// With several query rows per request a piece can hold no position that a row
+// sees; such a piece carries log-sum-exp -inf and weighs nothing, and a row
+// that no piece saw gets out = 0, lse = -inf.  The running maximum is kept at
+// or above kFloor, far below any real log-sum-exp, so that an empty piece
+// folds in with weight 2^-inf = 0 and never as -inf - (-inf): the fold has no
+// branch, and the loads of several pieces stay in flight together.
 #include "da_common.h"
 #include "da_launch.h"
 #include "da_plan.h"
@@ -20,6 +26,7 @@ namespace da {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr float kFloor = -3.0e38f;
 
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     __shared__ float4 part[kThreads];
@@ -29,6 +36,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     const int per_stream = a.group / nh;
     const int s = blockIdx.x / per_stream;
     const int h0 = (blockIdx.x % per_stream) * nh;
+    if ((h0 >> a.group_log2) >= a.rows) return;          // members that only pad the group
     const int b = s / a.units;
     const int j = s % a.units;
     // independent loads first: length, stream record, plan summary
@@ -51,10 +59,16 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     const int cols = C4 < kThreads ? C4 : kThreads;       // columns handled at once
     const int PL = kThreads / cols;                       // piece lanes per column
     const int q = t / cols;
-    const int64_t out_row = static_cast<int64_t>(b) * a.units * G + j * G + h0;
+    const int heads = a.units << a.group_log2;            // query heads per row
+    const int gmask = (1 << a.group_log2) - 1;
+    const int d4_log2 = __builtin_ctz(static_cast<unsigned>(D)) - 2;   // D is a power of two
     for (int c0 = 0; c0 < C4; c0 += cols) {
         const int c = c0 + t % cols;
-        const int h = (4 * c) / D;
+        const int h = c >> d4_log2;
+        const int cc = c - (h << d4_log2);                // float4 column within the head
+        const int slot_h = h0 + h;                        // (row, head) slot of the stream
+        const int r = slot_h >> a.group_log2;
+        const int64_t out_row = (static_cast<int64_t>(b) * a.rows + r) * heads + (j << a.group_log2) + (slot_h & gmask);
         float m = -__builtin_inff(), z = 0.0f;
         float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll 4
@@ -62,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
             const int64_t sl = slot_of(gf + i, start, W, A);
             const float l = a.lse_part[sl * G + h0 + h];
             const float4 o = reinterpret_cast<const float4*>(a.o_part + (sl * G + h0) * D)[c];
-            const float mn = fmaxf(m, l);
+            const float mn = fmaxf(fmaxf(m, l), kFloor);
             const float fo = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first piece
             const float fn = __builtin_amdgcn_exp2f(l - mn);
             z = z * fo + fn;
@@ -78,10 +92,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
             pz[t] = z;
             __syncthreads();
             if (q == 0) {
-                for (int r = 1; r < PL; ++r) {
-                    const int u = t + r * cols;
+                for (int pr = 1; pr < PL; ++pr) {
+                    const int u = t + pr * cols;
                     const float mo = pm[u];
-                    const float mn = fmaxf(m, mo);
+                    const float mn = fmaxf(fmaxf(m, mo), kFloor);
                     const float fs = __builtin_amdgcn_exp2f(m - mn);
                     const float fo = __builtin_amdgcn_exp2f(mo - mn);
                     const float4 o = part[u];
@@ -95,17 +109,18 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
             }
             __syncthreads();
         }
-        if (q == 0) {
-            const float inv = 1.0f / z;
+        if (q == 0 && r < a.rows) {
+            const float inv = z > 0.0f ? 1.0f / z : 0.0f;
             if (a.out_is_bf16) {
                 const uint32_t lo = f32_to_bf16_bits(acc.x * inv) | (static_cast<uint32_t>(f32_to_bf16_bits(acc.y * inv)) << 16);
                 const uint32_t hi = f32_to_bf16_bits(acc.z * inv) | (static_cast<uint32_t>(f32_to_bf16_bits(acc.w * inv)) << 16);
-                reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + out_row * D)[c] = make_uint2(lo, hi);
+                reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + out_row * D)[cc] = make_uint2(lo, hi);
             } else {
-                reinterpret_cast<float4*>(static_cast<float*>(a.out) + out_row * D)[c] =
+                reinterpret_cast<float4*>(static_cast<float*>(a.out) + out_row * D)[cc] =
                     make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
             }
-            if (a.lse != nullptr && (4 * c) % D == 0) a.lse[out_row + h] = (m + __builtin_log2f(z)) * kLn2;
+            if (a.lse != nullptr && cc == 0)
+                a.lse[out_row] = z > 0.0f ? (m + __builtin_log2f(z)) * kLn2 : -__builtin_inff();
         }
     }
 }

@@ -25,8 +25,8 @@ def lib():
 
 def test_header_declares_expected_entry_points():
     names = _declared()
-    for n in ("decode_attn_paged", "decode_attn_mla", "decode_attn_plan", "paged_kv_gather",
-              "decode_kv_append", "decode_kv_append_mla"):
+    for n in ("decode_attn_paged", "decode_attn_paged_rows", "decode_attn_mla", "decode_attn_plan",
+              "paged_kv_gather", "decode_kv_append", "decode_kv_append_mla"):
         assert n in names
 
 
@@ -151,3 +151,17 @@ def test_append_null_and_misaligned_rejected(lib):
     assert L.decode_kv_append_mla(ctypes.byref(md), FAKE + 8, FAKE, FAKE, FAKE, None) == -2
     md.latent_dim = 512
     assert L.decode_kv_append_mla(ctypes.byref(md), FAKE, FAKE, FAKE, FAKE, None) < 0
+
+
+@pytest.mark.parametrize("kw,rows,status", [
+    (dict(), 0, -2),                                   # no rows
+    (dict(), -1, -2),
+    (dict(), 9, -4),                                   # more rows than any kernel group holds
+    (dict(num_q_heads=8, num_kv_heads=2), 3, -4),      # 3 rows x 4 heads > 8 members
+    (dict(num_q_heads=8, num_kv_heads=1), 2, -4),      # 2 rows x 8 heads
+    (dict(head_dim=96), 2, -4),                        # descriptor checks still apply
+])
+def test_rows_rejected_before_any_device_call(lib, kw, rows, status):
+    d = _desc(lib, **kw)
+    st = lib.lib().decode_attn_paged_rows(ctypes.byref(d), rows, FAKE, FAKE, FAKE, FAKE, 1.0, FAKE, FAKE, None)
+    assert st == status

@@ -24,20 +24,25 @@ def mla_kv_bytes_per_token(latent_dim: int, elem_bytes: int = 2) -> int:
     return latent_dim * elem_bytes
 
 
-def gqa_bytes(seq_lens, page_size, q_heads, kv_heads, head_dim, q_dtype, kv_dtype) -> int:
+def gqa_bytes(seq_lens, page_size, q_heads, kv_heads, head_dim, q_dtype, kv_dtype, rows: int = 1) -> int:
+    """With ``rows`` query rows per request, q, out and lse grow by that factor;
+    the K/V history is still read once."""
     L = np.asarray(seq_lens, dtype=np.int64)
     B = len(L)
     pages = int(((L + page_size - 1) // page_size).sum())
     kv = int(L.sum()) * gqa_kv_bytes_per_token(kv_heads, head_dim, kv_dtype)
-    qb = B * q_heads * head_dim * ELEM_BYTES[q_dtype]
+    qb = rows * B * q_heads * head_dim * ELEM_BYTES[q_dtype]
     ob = qb                                   # out has q's dtype
-    lse = B * q_heads * 4
+    lse = rows * B * q_heads * 4
     scales = 2 * kv_heads * 4 if kv_dtype == FP8 else 0
     return kv + qb + ob + lse + 4 * pages + 4 * B + scales
 
 
-def gqa_flops(seq_lens, q_heads, head_dim) -> int:
-    return int(np.asarray(seq_lens, dtype=np.int64).sum()) * q_heads * 2 * (head_dim + head_dim)
+def gqa_flops(seq_lens, q_heads, head_dim, rows: int = 1) -> int:
+    """Row i of n sees L - n + 1 + i positions."""
+    L = np.asarray(seq_lens, dtype=np.int64)
+    seen = sum(int(np.maximum(L - rows + 1 + i, 0).sum()) for i in range(rows))
+    return seen * q_heads * 2 * (head_dim + head_dim)
 
 
 def mla_bytes(seq_lens, page_size, q_heads, latent_dim, v_dim) -> int:
