@@ -35,12 +35,12 @@ from .attention import (gather_history, paged_decode_attention, mla_decode_atten
                         attention_over_range, lse_merge, dense_attention)
 from .plan import partition, Partition
 from .append import fp8_e4m3fn_encode, kv_append, mla_kv_append
-from .rows import paged_decode_attention_rows, visible_tokens
+from .rows import paged_decode_attention_rows, mla_decode_attention_rows, visible_tokens
 
 __all__ = [
     "bf16_bits_to_f64", "fp8_e4m3fn_to_f64", "fp8_e4m3fn_table", "decode_storage",
     "gather_history", "paged_decode_attention", "mla_decode_attention",
     "attention_over_range", "lse_merge", "dense_attention", "partition", "Partition",
     "fp8_e4m3fn_encode", "kv_append", "mla_kv_append",
-    "paged_decode_attention_rows", "visible_tokens",
+    "paged_decode_attention_rows", "mla_decode_attention_rows", "visible_tokens",
 ]

@@ -17,7 +17,8 @@ Readings where the pages are silent (numbered after those of append.py):
     history whole; among the new rows the mask is causal.
 14. q and out are [B][n][Hq][D] (a request's rows in position order, heads
     inside a row as in the single-row case), lse is [B][n][Hq]; one call has
-    one n for every request.
+    one n for every request.  MLA likewise: q [B][n][H][576], out
+    [B][n][H][512], every row over the head-shared latent.
 15. A row that sees no position (L - n + i < 0, possible only when L < n)
     gives out = 0 and lse = -inf, as an empty history does (reading 5).
 """
@@ -28,7 +29,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 from .attention import gather_history, dense_attention, _dequant
-from .formats import decode_storage
+from .formats import decode_storage, BF16
 
 
 def visible_tokens(L: int, n: int, i: int) -> int:
@@ -64,4 +65,29 @@ def paged_decode_attention_rows(q, q_dtype: int, kv_pages, kv_dtype: int, page_t
                 o, l = dense_attention(qf[b, i, j * g:(j + 1) * g], K[:vis, j, :], V[:vis, j, :], scale)
                 out[b, i, j * g:(j + 1) * g] = o
                 lse[b, i, j * g:(j + 1) * g] = l
+    return out, lse
+
+
+def mla_decode_attention_rows(q_bits, kv_bits, page_table, seq_lens, page_size: int, scale: float,
+                              v_dim: int = 512, requests: Optional[Sequence[int]] = None):
+    """Absorbed MLA decode with n query rows per request (readings 13-15).  q
+    [B][n][H][576] and pages [num_pages][P][576] as bf16 bit patterns; returns
+    float64 out [B][n][H][v_dim] and lse [B][n][H]."""
+    qf = decode_storage(q_bits, BF16)
+    B, n, H, Dk = qf.shape
+    out = np.full((B, n, H, v_dim), np.nan)
+    lse = np.full((B, n, H), np.nan)
+    for b in (range(B) if requests is None else requests):
+        L = int(seq_lens[b])
+        if L > 0:
+            C = decode_storage(gather_history(kv_bits, page_table, b, L, page_size, mla=True), BF16)
+        for i in range(n):
+            vis = visible_tokens(L, n, i)
+            if vis == 0:
+                out[b, i] = 0.0
+                lse[b, i] = -np.inf
+                continue
+            o, l = dense_attention(qf[b, i], C[:vis], C[:vis, :v_dim], scale)
+            out[b, i] = o
+            lse[b, i] = l
     return out, lse

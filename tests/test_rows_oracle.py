@@ -177,3 +177,73 @@ def test_planted_mask_mistakes_are_caught(monkeypatch, planted):
     out, lse = _run(c, 0.2)
     bad = np.nanmax(np.abs(out - good[0]))
     assert not np.isfinite(bad) or bad > 1e-6
+
+
+# ---- MLA: every row over the head-shared latent, keys 576 wide, values its first 512
+
+def _mla_case(rng, B, n, H, lens, P=64, Dk=576):
+    lens = np.asarray(lens, dtype=np.int32)
+    npg = (lens + P - 1) // P
+    num_pages = int(npg.sum()) + 2
+    perm = rng.permutation(num_pages).astype(np.int32)
+    table = np.full((B, max(1, int(npg.max()))), -1, dtype=np.int32)
+    at = 0
+    for b in range(B):
+        table[b, :npg[b]] = perm[at:at + npg[b]]
+        at += npg[b]
+    q = wl.to_bf16_bits((0.5 * rng.standard_normal((B, n, H, Dk))).astype(np.float32))
+    kv = wl.to_bf16_bits((0.5 * rng.standard_normal((num_pages, P, Dk))).astype(np.float32))
+    return q, kv, table, lens, P
+
+
+def _mla_latent(kv, table, b, L, P):
+    C = np.zeros((L, kv.shape[2]))
+    for t in range(L):
+        C[t] = oracle.decode_storage(kv[table[b, t // P], t % P], BF16)
+    return C
+
+
+def test_mla_every_token_a_row_equals_torch_causal_sdpa():
+    rng = np.random.default_rng(31)
+    n, H = 19, 8
+    q, kv, table, lens, P = _mla_case(rng, 2, n, H, [n, n], P=16)
+    scale = 1 / np.sqrt(576)
+    out, lse = oracle.mla_decode_attention_rows(q, kv, table, lens, P, scale)
+    qf = oracle.decode_storage(q, BF16)
+    for b in range(2):
+        C = _mla_latent(kv, table, b, n, P)
+        qt = torch.from_numpy(qf[b].transpose(1, 0, 2).copy())[None]                     # [1][H][n][576]
+        kt = torch.from_numpy(C).expand(H, n, 576)[None]
+        vt = torch.from_numpy(C[:, :512].copy()).expand(H, n, 512)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=scale)
+        assert np.max(np.abs(out[b] - ref[0].numpy().transpose(1, 0, 2))) < 1e-12
+
+
+def test_mla_rows_match_triangular_mask_brute_force():
+    rng = np.random.default_rng(32)
+    n, H = 2, 4
+    lens = [0, 1, 2, 64, 65, 130]
+    q, kv, table, lens, P = _mla_case(rng, len(lens), n, H, lens)
+    scale = 0.05
+    out, lse = oracle.mla_decode_attention_rows(q, kv, table, lens, P, scale)
+    qf = oracle.decode_storage(q, BF16)
+    for b, L in enumerate(lens):
+        C = _mla_latent(kv, table, b, int(L), P)
+        keep = np.tril(np.ones((n, int(L)), dtype=bool), k=int(L) - n)
+        for h in range(H):
+            S = np.where(keep, scale * (qf[b, :, h, :] @ C.T), -np.inf) if L else np.zeros((n, 0))
+            for i in range(n):
+                if L == 0 or not keep[i].any():
+                    assert np.all(out[b, i, h] == 0.0) and lse[b, i, h] == -np.inf
+                    continue
+                p = scipy.special.softmax(S[i])
+                assert np.max(np.abs(out[b, i, h] - p @ C[:, :512])) < 1e-12
+                assert abs(lse[b, i, h] - scipy.special.logsumexp(S[i])) < 1e-12
+
+
+def test_mla_single_row_is_the_decode_oracle():
+    rng = np.random.default_rng(33)
+    q, kv, table, lens, P = _mla_case(rng, 3, 1, 8, [1, 64, 100])
+    out, lse = oracle.mla_decode_attention_rows(q, kv, table, lens, P, 0.04)
+    ro, rl = oracle.mla_decode_attention(q[:, 0], kv, table, lens, P, 0.04)
+    assert np.array_equal(out[:, 0], ro) and np.array_equal(lse[:, 0], rl)
