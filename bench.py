@@ -266,8 +266,44 @@ class RowsRunner(GqaRunner):
         return self.rows * len(self.case.seq_lens)       # tokens decoded per step
 
 
+class MlaRowsRunner(MlaRunner):
+    """The MLA workload with several query rows per request (multi-token
+    prediction): q [B][rows][H][576], out [B][rows][H][512]."""
+
+    def __init__(self, cfg, rows, sets=2):
+        import numpy as np
+        import workloads as wl
+        from workloads import accounting
+        super().__init__(cfg, sets)
+        self.rows = rows
+        c = self.case
+        B, H = c.q.shape[:2]
+        rng = np.random.default_rng(wl.BASE_SEED + rows)
+        q32 = (cfg.value_std * rng.standard_normal((B, rows, H, cfg.latent_dim))).astype(np.float32)
+        self.q = _to_dev(wl.to_bf16_bits(q32), wl.BF16, "cuda")
+        self.out = self.out.new_empty((B, rows, H, cfg.v_dim))
+        self.lse = self.lse.new_empty((B, rows, H))
+        self.bytes = accounting.mla_bytes(c.seq_lens, cfg.page_size, H, cfg.latent_dim, cfg.v_dim, rows)
+        self.flops = accounting.mla_flops(c.seq_lens, H, cfg.latent_dim, cfg.v_dim, rows)
+
+    def step(self):
+        import paged_kv_cache_471_amd as da
+        kv = self.kvs[self.i % len(self.kvs)]
+        self.i += 1
+        da.decode_attn_mla_rows(self.q, kv, self.pt, self.sl, self.case.scale, self.cfg.v_dim, self.out, self.lse)
+
+    @property
+    def batch(self):
+        return self.rows * len(self.case.seq_lens)       # tokens decoded per step
+
+
 # secondary workloads with several query rows per request: name -> (workload, rows)
-ROWS_WORKLOADS = {"llama8b-mtp2": ("llama8b", 2)}
+ROWS_WORKLOADS = {"llama8b-mtp2": ("llama8b", 2), "mla-mtp2": ("mla", 2)}
+
+
+def rows_runner(cfg, rows):
+    import workloads as wl
+    return MlaRowsRunner(cfg, rows) if isinstance(cfg, wl.MLAConfig) else RowsRunner(cfg, rows)
 
 
 def make_runner(cfg):
@@ -354,7 +390,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b")
-    ap.add_argument("--secondary", default="skewed,mla,longfp8,llama8b-mtp2",
+    ap.add_argument("--secondary", default="skewed,mla,longfp8,llama8b-mtp2,mla-mtp2",
                     help="comma list of other workloads to report beside the headline ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -382,7 +418,7 @@ def main():
     if args.workload in ROWS_WORKLOADS:
         base_name, rows = ROWS_WORKLOADS[args.workload]
         cfg = wl.CONFIGS[base_name]
-        runner = RowsRunner(cfg, rows)
+        runner = rows_runner(cfg, rows)
     else:
         cfg = wl.CONFIGS[args.workload]
         runner = make_runner(cfg)
@@ -445,7 +481,7 @@ def main():
             scfg = wl.CONFIGS[name]
         del runner
         torch.cuda.empty_cache()
-        runner2 = RowsRunner(scfg, rows) if rows > 1 else make_runner(scfg)
+        runner2 = rows_runner(scfg, rows) if rows > 1 else make_runner(scfg)
         print(f"# secondary {name}: sum L = {runner2.tokens}, {runner2.bytes / 1e6:.1f} MB", file=sys.stderr,
               flush=True)
         sms, skms, _ = time_runner(runner2, max(10, args.steps // 2), max(3, args.warmup // 2), warm_s=SETTLE_S)

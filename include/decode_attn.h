@@ -177,6 +177,25 @@ int decode_attn_paged_rows(const da_paged_desc* desc, int32_t q_rows, const void
 int decode_attn_mla(const da_mla_desc* desc, const void* q, const void* kv_pages,
                     const int32_t* page_table, const int32_t* seq_lens, float scale,
                     void* out, float* lse, void* stream);
+
+/*
+ * decode_attn_mla_rows - decode_attn_mla with q_rows query rows per request
+ * (the DeepSeek-V3 configuration decodes with multi-token prediction of depth
+ * 1, two rows per request: "Analytical Provisioning", App. B.1; a request's
+ * query rows q_i: "OpWeave", §4.2).  Row i of request b sees latent positions
+ * t <= seq_lens[b] - q_rows + i; a row that sees none gets out = 0, lse = -inf.
+ *   q_rows      >= 1, with batch * q_rows <= 8192.
+ *   q           device, bf16 [B][q_rows][heads][576].
+ *   out         device, bf16 [B][q_rows][heads][512] (written).
+ *   lse         device, fp32 [B][q_rows][heads] (written), or NULL.
+ * Each row runs as a request of its own over request b's pages (a small
+ * kernel writes the rows' lengths and page tables into the library's
+ * workspace first), so the latent is read once per row.  Other arguments and
+ * errors as decode_attn_mla.
+ */
+int decode_attn_mla_rows(const da_mla_desc* desc, int32_t q_rows, const void* q, const void* kv_pages,
+                         const int32_t* page_table, const int32_t* seq_lens, float scale,
+                         void* out, float* lse, void* stream);
 /*
  * decode_kv_append - write this step's new token into each request's paged
  * history (the history grows by one token per decode step and is then read

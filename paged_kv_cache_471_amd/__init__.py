@@ -21,7 +21,7 @@ DA_F32, DA_BF16, DA_FP8_E4M3 = 0, 1, 2
 STATUS = {0: "DA_OK", -1: "DA_ERR_NULL", -2: "DA_ERR_SHAPE", -3: "DA_ERR_DTYPE", -4: "DA_ERR_UNSUPPORTED",
           -5: "DA_ERR_WORKSPACE", -6: "DA_ERR_HIP"}
 
-EXPORTS = ("decode_attn_paged", "decode_attn_paged_rows", "decode_attn_mla", "decode_attn_plan", "paged_kv_gather",
+EXPORTS = ("decode_attn_paged", "decode_attn_paged_rows", "decode_attn_mla", "decode_attn_mla_rows", "decode_attn_plan", "paged_kv_gather",
            "decode_kv_append", "decode_kv_append_mla",
            "decode_attn_default_workers", "decode_attn_status_str", "decode_attn_last_hip_error",
            "decode_attn_timer_begin", "decode_attn_timer_end")
@@ -61,6 +61,8 @@ def _load():
     lib.decode_attn_paged_rows.restype = ctypes.c_int
     lib.decode_attn_mla.argtypes = [ctypes.POINTER(MLADesc), vp, vp, vp, vp, f32, vp, vp, vp]
     lib.decode_attn_mla.restype = ctypes.c_int
+    lib.decode_attn_mla_rows.argtypes = [ctypes.POINTER(MLADesc), i32, vp, vp, vp, vp, f32, vp, vp, vp]
+    lib.decode_attn_mla_rows.restype = ctypes.c_int
     lib.decode_attn_plan.argtypes = [i32, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
     lib.decode_attn_plan.restype = ctypes.c_int
     lib.paged_kv_gather.argtypes = [ctypes.POINTER(PagedDesc), i32, vp, vp, vp, vp, vp]
@@ -203,6 +205,30 @@ def decode_attn_mla(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.T
     return out, lse
 
 
+def decode_attn_mla_rows(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor,
+                         seq_lens: torch.Tensor, scale: float, v_dim: int = 512, out: Optional[torch.Tensor] = None,
+                         lse: Optional[torch.Tensor] = None, *, workers: int = 0, want_lse: bool = True,
+                         stream=None):
+    """Absorbed MLA decode with several query rows per request.  q bf16
+    [B][n][H][576]: row i of request b sees latent positions up to
+    seq_lens[b] - n + i.  Returns (out bf16 [B][n][H][v_dim], lse fp32 [B][n][H] or None)."""
+    _need_cuda(q, kv_pages, page_table, seq_lens)
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B][rows][H][576], got {tuple(q.shape)}")
+    B, n, H, Dk = q.shape
+    if out is None:
+        out = torch.empty((B, n, H, v_dim), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, n, H), dtype=torch.float32, device=q.device)
+    _need_cuda(out, lse)
+    num_pages, P, Dk2 = kv_pages.shape
+    d = MLADesc(B, H, Dk, v_dim, P, num_pages, page_table.shape[1], workers)
+    st = _lib.decode_attn_mla_rows(ctypes.byref(d), n, _ptr(q), _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens),
+                                   float(scale), _ptr(out), _ptr(lse), _stream(stream))
+    _check(st, "decode_attn_mla_rows")
+    return out, lse
+
+
 def decode_attn_plan(seq_lens: torch.Tensor, page_size: int, units: int, workers: int, stream=None):
     """Run the split-KV planner alone; returns its outputs as int32 tensors."""
     _need_cuda(seq_lens)
@@ -298,5 +324,6 @@ def timer_end():
     return ms.value, n.value
 
 
-__all__ = ["timer_begin", "timer_end", "decode_attn_paged", "decode_attn_paged_rows", "decode_attn_mla", "decode_attn_plan", "paged_kv_gather", "default_workers",
+__all__ = ["timer_begin", "timer_end", "decode_attn_paged", "decode_attn_paged_rows", "decode_attn_mla",
+           "decode_attn_mla_rows", "decode_attn_plan", "paged_kv_gather", "default_workers",
            "PagedDesc", "MLADesc", "DecodeAttnError", "LIB_PATH", "EXPORTS", "lib", "decode_kv_append", "decode_kv_append_mla"]

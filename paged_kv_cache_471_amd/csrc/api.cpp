@@ -13,6 +13,7 @@
 
 #include "../../include/decode_attn.h"
 #include "da_append.h"
+#include "da_rows.h"
 
 namespace {
 
@@ -77,9 +78,10 @@ struct SplitBuffers {
     int2* stream_info;
     float* o_part;
     float* lse_part;
+    int32_t* extra;         // extra_ints int32 values for the caller (multi-row expansion)
 };
 
-size_t split_layout(int streams, int G, int heads, int dim, char* base, SplitBuffers* sb) {
+size_t split_layout(int streams, int G, int heads, int dim, char* base, SplitBuffers* sb, size_t extra_ints = 0) {
     size_t off = 0;
     auto take = [&](size_t bytes) -> char* {
         char* p = base ? base + off : nullptr;
@@ -91,15 +93,17 @@ size_t split_layout(int streams, int G, int heads, int dim, char* base, SplitBuf
     t.stream_info = reinterpret_cast<int2*>(take(sizeof(int2) * static_cast<size_t>(streams)));
     t.o_part = reinterpret_cast<float*>(take(sizeof(float) * 2 * static_cast<size_t>(G) * heads * dim));
     t.lse_part = reinterpret_cast<float*>(take(sizeof(float) * 2 * static_cast<size_t>(G) * heads));
+    t.extra = extra_ints ? reinterpret_cast<int32_t*>(take(sizeof(int32_t) * extra_ints)) : nullptr;
     if (sb) *sb = t;
     return off;
 }
 
-int get_split_buffers(hipStream_t s, int streams, int G, int heads, int dim, SplitBuffers* sb) {
+int get_split_buffers(hipStream_t s, int streams, int G, int heads, int dim, SplitBuffers* sb,
+                      size_t extra_ints = 0) {
     void* base = nullptr;
-    int st = get_workspace(s, split_layout(streams, G, heads, dim, nullptr, nullptr), &base);
+    int st = get_workspace(s, split_layout(streams, G, heads, dim, nullptr, nullptr, extra_ints), &base);
     if (st != DA_OK) return st;
-    split_layout(streams, G, heads, dim, static_cast<char*>(base), sb);
+    split_layout(streams, G, heads, dim, static_cast<char*>(base), sb, extra_ints);
     return DA_OK;
 }
 
@@ -317,6 +321,92 @@ int gqa_step(const da_paged_desc* d, int q_rows, const void* q, const void* kv_p
     return DA_OK;
 }
 
+// One MLA step with q_rows query rows per request.  Several rows run as
+// batch * q_rows requests (rows.hip writes their lengths and page tables into
+// the workspace); q, out and lse [batch][q_rows][heads][...] are already laid
+// out as those requests.
+int mla_step(const da_mla_desc* dd, int q_rows, const void* q, const void* kv_pages, const int32_t* page_table,
+             const int32_t* seq_lens, float scale, void* out, float* lse, void* stream) {
+    int st = check_mla(dd);
+    if (st != DA_OK) return st;
+    if (q_rows < 1) return DA_ERR_SHAPE;
+    da_mla_desc rd = *dd;
+    rd.batch = dd->batch * q_rows;
+    if (rd.batch > da::kMaxBatch) return DA_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(rd.batch) * rd.max_pages_per_seq >= (int64_t(1) << 31)) return DA_ERR_UNSUPPORTED;
+    const da_mla_desc* d = &rd;
+    if (q == nullptr || kv_pages == nullptr || page_table == nullptr || seq_lens == nullptr || out == nullptr)
+        return DA_ERR_NULL;
+    if (!aligned(kv_pages, 16) || !aligned(q, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
+        !aligned(page_table, 4) || !aligned(seq_lens, 4))
+        return DA_ERR_SHAPE;
+    if (!(scale == scale)) return DA_ERR_SHAPE;
+    if (d->batch == 0) return DA_OK;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int G = 0;
+    st = resolve_mla_workers(d, &G);
+    if (st != DA_OK) return st;
+    SplitBuffers sb;
+    const size_t extra = q_rows > 1 ? static_cast<size_t>(d->batch) * (1 + d->max_pages_per_seq) : 0;
+    st = get_split_buffers(s, d->batch, G, d->num_heads, d->v_dim, &sb, extra);
+    if (st != DA_OK) return st;
+    if (q_rows > 1) {
+        da::RowsArgs ra{};
+        ra.seq_lens = seq_lens;
+        ra.page_table = page_table;
+        ra.lens_out = sb.extra;
+        ra.table_out = sb.extra + d->batch;
+        ra.batch = dd->batch;
+        ra.rows = q_rows;
+        ra.page_size = d->page_size;
+        ra.max_pages = d->max_pages_per_seq;
+        hipError_t e = da::launch_rows_expand(ra, s);
+        if (e != hipSuccess) return hip_fail(e);
+        seq_lens = ra.lens_out;
+        page_table = ra.table_out;
+    }
+
+    da::MlaArgs ma{};
+    ma.q = q;
+    ma.kv = kv_pages;
+    ma.page_table = page_table;
+    ma.seq_lens = seq_lens;
+    ma.scale_log2 = scale * 1.4426950408889634f;
+    ma.batch = d->batch;
+    ma.heads = d->num_heads;
+    ma.page_size = d->page_size;
+    ma.max_pages = d->max_pages_per_seq;
+    ma.workers = G;
+    ma.plan_info = sb.plan_info;
+    ma.stream_info = sb.stream_info;
+    ma.out = out;
+    ma.lse = lse;
+    ma.o_part = sb.o_part;
+    ma.lse_part = sb.lse_part;
+    hipError_t e = da::launch_mla(ma, s, next_kernel_events());
+    if (e != hipSuccess) return hip_fail(e);
+
+    da::MergeArgs mg{};
+    mg.seq_lens = seq_lens;
+    mg.plan_info = sb.plan_info;
+    mg.stream_info = sb.stream_info;
+    mg.o_part = sb.o_part;
+    mg.lse_part = sb.lse_part;
+    mg.out = out;
+    mg.lse = lse;
+    mg.units = 1;
+    mg.group = d->num_heads;
+    mg.dim = d->v_dim;
+    mg.rows = 1;
+    mg.group_log2 = __builtin_ctz(static_cast<unsigned>(d->num_heads));
+    mg.heads_per_block = d->num_heads >= 8 ? 8 : d->num_heads;
+    mg.out_is_bf16 = 1;
+    e = da::launch_merge(mg, d->batch, s);
+    if (e != hipSuccess) return hip_fail(e);
+    return DA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -388,62 +478,13 @@ int decode_attn_paged_rows(const da_paged_desc* d, int32_t q_rows, const void* q
 
 int decode_attn_mla(const da_mla_desc* d, const void* q, const void* kv_pages, const int32_t* page_table,
                     const int32_t* seq_lens, float scale, void* out, float* lse, void* stream) {
-    int st = check_mla(d);
-    if (st != DA_OK) return st;
-    if (q == nullptr || kv_pages == nullptr || page_table == nullptr || seq_lens == nullptr || out == nullptr)
-        return DA_ERR_NULL;
-    if (!aligned(kv_pages, 16) || !aligned(q, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
-        !aligned(page_table, 4) || !aligned(seq_lens, 4))
-        return DA_ERR_SHAPE;
-    if (!(scale == scale)) return DA_ERR_SHAPE;
-    if (d->batch == 0) return DA_OK;
+    return mla_step(d, 1, q, kv_pages, page_table, seq_lens, scale, out, lse, stream);
+}
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    int G = 0;
-    st = resolve_mla_workers(d, &G);
-    if (st != DA_OK) return st;
-    SplitBuffers sb;
-    st = get_split_buffers(s, d->batch, G, d->num_heads, d->v_dim, &sb);
-    if (st != DA_OK) return st;
-
-    da::MlaArgs ma{};
-    ma.q = q;
-    ma.kv = kv_pages;
-    ma.page_table = page_table;
-    ma.seq_lens = seq_lens;
-    ma.scale_log2 = scale * 1.4426950408889634f;
-    ma.batch = d->batch;
-    ma.heads = d->num_heads;
-    ma.page_size = d->page_size;
-    ma.max_pages = d->max_pages_per_seq;
-    ma.workers = G;
-    ma.plan_info = sb.plan_info;
-    ma.stream_info = sb.stream_info;
-    ma.out = out;
-    ma.lse = lse;
-    ma.o_part = sb.o_part;
-    ma.lse_part = sb.lse_part;
-    hipError_t e = da::launch_mla(ma, s, next_kernel_events());
-    if (e != hipSuccess) return hip_fail(e);
-
-    da::MergeArgs mg{};
-    mg.seq_lens = seq_lens;
-    mg.plan_info = sb.plan_info;
-    mg.stream_info = sb.stream_info;
-    mg.o_part = sb.o_part;
-    mg.lse_part = sb.lse_part;
-    mg.out = out;
-    mg.lse = lse;
-    mg.units = 1;
-    mg.group = d->num_heads;
-    mg.dim = d->v_dim;
-    mg.rows = 1;
-    mg.group_log2 = __builtin_ctz(static_cast<unsigned>(d->num_heads));
-    mg.heads_per_block = d->num_heads >= 8 ? 8 : d->num_heads;
-    mg.out_is_bf16 = 1;
-    e = da::launch_merge(mg, d->batch, s);
-    if (e != hipSuccess) return hip_fail(e);
-    return DA_OK;
+int decode_attn_mla_rows(const da_mla_desc* d, int32_t q_rows, const void* q, const void* kv_pages,
+                         const int32_t* page_table, const int32_t* seq_lens, float scale, void* out, float* lse,
+                         void* stream) {
+    return mla_step(d, q_rows, q, kv_pages, page_table, seq_lens, scale, out, lse, stream);
 }
 
 int decode_kv_append(const da_paged_desc* d, const void* k_new, const void* v_new, void* kv_pages,

@@ -1,0 +1,40 @@
+// Several query rows per request on the absorbed MLA path.
+//
+// A request's query rows in a step are one in plain decode, two with
+// multi-token prediction of depth 1 ("OpWeave", §4.2, the rows q_i of each
+// request; "Analytical Provisioning", App. B.1, the DeepSeek-V3 configuration
+// with MTP depth 1).  The rows are the last ones of the history and row i sees
+// positions up to its own, so each row is a decode query over a history cut
+// at its own length.  This kernel writes, for each row, that length and a copy
+// of the request's page-table entries the row reads; the MLA attention and
+// merge kernels then run unchanged over batch * rows requests, whose queries
+// and outputs [batch][rows][heads][...] already sit in that order.
+#include "da_common.h"
+#include "da_rows.h"
+
+namespace da {
+namespace {
+
+constexpr int kRowsBlock = 128;
+
+__global__ __launch_bounds__(kRowsBlock) void rows_expand_kernel(RowsArgs a) {
+    const int r = blockIdx.x;                   // expanded request b * rows + i
+    const int b = r / a.rows;
+    const int i = r - b * a.rows;
+    const int L = a.seq_lens[b];
+    const int len = max(0, L - a.rows + 1 + i);
+    if (threadIdx.x == 0) a.lens_out[r] = len;
+    const int pages = (len + a.page_size - 1) / a.page_size;
+    const int32_t* src = a.page_table + static_cast<int64_t>(b) * a.max_pages;
+    int32_t* dst = a.table_out + static_cast<int64_t>(r) * a.max_pages;
+    for (int p = threadIdx.x; p < pages; p += kRowsBlock) dst[p] = src[p];
+}
+
+}  // namespace
+
+hipError_t launch_rows_expand(const RowsArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(rows_expand_kernel, dim3(a.batch * a.rows), dim3(kRowsBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace da

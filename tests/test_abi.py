@@ -25,7 +25,7 @@ def lib():
 
 def test_header_declares_expected_entry_points():
     names = _declared()
-    for n in ("decode_attn_paged", "decode_attn_paged_rows", "decode_attn_mla", "decode_attn_plan",
+    for n in ("decode_attn_paged", "decode_attn_paged_rows", "decode_attn_mla", "decode_attn_mla_rows", "decode_attn_plan",
               "paged_kv_gather", "decode_kv_append", "decode_kv_append_mla"):
         assert n in names
 
@@ -165,3 +165,13 @@ def test_rows_rejected_before_any_device_call(lib, kw, rows, status):
     d = _desc(lib, **kw)
     st = lib.lib().decode_attn_paged_rows(ctypes.byref(d), rows, FAKE, FAKE, FAKE, FAKE, 1.0, FAKE, FAKE, None)
     assert st == status
+
+
+def test_mla_rows_rejected_before_any_device_call(lib):
+    good = dict(batch=4, num_heads=128, latent_dim=576, v_dim=512, page_size=64, num_pages=10,
+                max_pages_per_seq=4, workers=0)
+    f = lib.lib().decode_attn_mla_rows
+    for kw, rows, status in [(dict(), 0, -2), (dict(), -3, -2), (dict(batch=4096), 3, -4),
+                             (dict(num_heads=96), 2, -4)]:
+        d = lib.MLADesc(**{**good, **kw})
+        assert f(ctypes.byref(d), rows, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, None) == status

@@ -45,19 +45,24 @@ def gqa_flops(seq_lens, q_heads, head_dim, rows: int = 1) -> int:
     return seen * q_heads * 2 * (head_dim + head_dim)
 
 
-def mla_bytes(seq_lens, page_size, q_heads, latent_dim, v_dim) -> int:
+def mla_bytes(seq_lens, page_size, q_heads, latent_dim, v_dim, rows: int = 1) -> int:
+    """With ``rows`` query rows per request, q, out and lse grow by that factor;
+    the latent history is counted once, as the method needs it once."""
     L = np.asarray(seq_lens, dtype=np.int64)
     B = len(L)
     pages = int(((L + page_size - 1) // page_size).sum())
     kv = int(L.sum()) * mla_kv_bytes_per_token(latent_dim)
-    qb = B * q_heads * latent_dim * 2
-    ob = B * q_heads * v_dim * 2
-    lse = B * q_heads * 4
+    qb = rows * B * q_heads * latent_dim * 2
+    ob = rows * B * q_heads * v_dim * 2
+    lse = rows * B * q_heads * 4
     return kv + qb + ob + lse + 4 * pages + 4 * B
 
 
-def mla_flops(seq_lens, q_heads, latent_dim, v_dim) -> int:
-    return int(np.asarray(seq_lens, dtype=np.int64).sum()) * q_heads * 2 * (latent_dim + v_dim)
+def mla_flops(seq_lens, q_heads, latent_dim, v_dim, rows: int = 1) -> int:
+    """Row i of n sees L - n + 1 + i positions."""
+    L = np.asarray(seq_lens, dtype=np.int64)
+    seen = sum(int(np.maximum(L - rows + 1 + i, 0).sum()) for i in range(rows))
+    return seen * q_heads * 2 * (latent_dim + v_dim)
 
 
 __all__ = ["gqa_kv_bytes_per_token", "mla_kv_bytes_per_token", "gqa_bytes", "gqa_flops",
