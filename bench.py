@@ -24,6 +24,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -306,6 +307,106 @@ def rows_runner(cfg, rows):
     return MlaRowsRunner(cfg, rows) if isinstance(cfg, wl.MLAConfig) else RowsRunner(cfg, rows)
 
 
+# ---------------------------------------------------------------- latency model
+
+# Slot traces for the calibration: prompts and decode lifetimes per slot; the
+# batch at a decode step far into the traces holds each slot's stationary load.
+CALIB = {
+    "gqa": dict(shape=dict(q_heads=32, kv_heads=8, head_dim=128, page_size=16), slots=(16, 32, 64, 128, 256),
+                p_law="lognormal:1024:0.8:16:16384", d_law="geometric:512"),
+    "mla": dict(shape=dict(heads=128, page_size=64), slots=(32, 64, 96, 128, 192),
+                p_law="lognormal:2048:0.8:64:32768", d_law="geometric:512"),
+}
+
+
+class CalibRunner:
+    """One decode step over a batch of stationary slot loads, on a K/V buffer
+    filled on the device (values do not change the time)."""
+
+    def __init__(self, kind, lens, kv, gen):
+        import numpy as np
+        import torch
+        c = CALIB[kind]["shape"]
+        self.kind = kind
+        B = len(lens)
+        P = c["page_size"]
+        npg = (lens + P - 1) // P
+        width = int(npg.max())
+        table = np.full((B, width), -1, dtype=np.int32)
+        perm = np.random.default_rng(int(lens.sum())).permutation(int(npg.sum())).astype(np.int32)
+        at = 0
+        for b in range(B):
+            table[b, :npg[b]] = perm[at:at + npg[b]]
+            at += int(npg[b])
+        self.pt = torch.from_numpy(table).cuda()
+        self.sl = torch.from_numpy(lens.astype(np.int32)).cuda()
+        self.kv = kv
+        if kind == "gqa":
+            self.q = torch.randn((B, c["q_heads"], c["head_dim"]), generator=gen, device="cuda").to(torch.bfloat16)
+            self.scale = c["head_dim"] ** -0.5
+        else:
+            self.q = (0.5 * torch.randn((B, c["heads"], 576), generator=gen, device="cuda")).to(torch.bfloat16)
+            self.scale = 576 ** -0.5
+        self.out = self.lse = None
+
+    def step(self):
+        import paged_kv_cache_471_amd as da
+        if self.kind == "gqa":
+            self.out, self.lse = da.decode_attn_paged(self.q, self.kv, self.pt, self.sl, self.scale, self.out, self.lse)
+        else:
+            self.out, self.lse = da.decode_attn_mla(self.q, self.kv, self.pt, self.sl, self.scale, 512, self.out,
+                                                    self.lse)
+
+
+def calibrate_latency(kind, steps=20, warmup=5):
+    """Fit t_A(T) = alpha_A T + beta_A for one head shape from the kernel's own
+    time and the whole step's, over batches of stationary slot loads."""
+    import numpy as np
+    import torch
+    import workloads as wl
+    import workloads.slots as slots
+    from paged_kv_cache_471_amd import provision
+    c = CALIB[kind]
+    Bmax = max(c["slots"])
+    Pt, Dt = slots.draw_slot_traces(Bmax, 400, c["p_law"], c["d_law"], k=1 if kind == "gqa" else 2)
+    theta, q2, nu2 = provision.trace_moments(Pt.ravel(), Dt.ravel())
+    step_at = 40 * int(Dt.mean())                   # many lifetimes into every slot's trace
+    loads = provision.slot_loads(Pt, Dt, step_at)
+    sh = c["shape"]
+    P = sh["page_size"]
+    pages = int(((loads + P - 1) // P).sum()) + 1
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.BASE_SEED + 7)
+    if kind == "gqa":
+        kv = torch.randn((pages, 2, sh["kv_heads"], P, sh["head_dim"]), generator=gen, device="cuda").to(torch.bfloat16)
+        per_token = 2 * sh["kv_heads"] * sh["head_dim"] * 2
+    else:
+        kv = (0.5 * torch.randn((pages, P, 576), generator=gen, device="cuda")).to(torch.bfloat16)
+        per_token = 576 * 2
+    pts = []
+    for B in c["slots"]:
+        lens = loads[:B].astype(np.int64)
+        r = CalibRunner(kind, lens, kv, gen)
+        ms, kms, _ = time_runner(r, steps, warmup, warm_s=0.1)
+        pts.append(dict(slots=B, T=int(lens.sum()), step_us=round(ms * 1e3, 2), kernel_us=round(kms * 1e3, 2)))
+        del r
+    T = [p["T"] for p in pts]
+    ak, bk, r2k = provision.fit_latency(T, [p["kernel_us"] * 1e-6 for p in pts])
+    a_s, b_s, r2s = provision.fit_latency(T, [p["step_us"] * 1e-6 for p in pts])
+    del kv
+    torch.cuda.empty_cache()
+    return {
+        "shape": sh, "bytes_per_token": per_token,
+        "slot_traces": {"prompt": c["p_law"], "lifetime": c["d_law"], "theta_hat": round(theta, 1),
+                        "nu_hat": round(math.sqrt(nu2), 1), "mean_load_at_step": round(float(loads.mean()), 1)},
+        "points": pts,
+        "kernel": {"alpha_ns_per_token": round(ak * 1e9, 5), "beta_us": round(bk * 1e6, 2), "r2": round(r2k, 5),
+                   "effective_GBps": round(per_token / ak / 1e9, 1)},
+        "step": {"alpha_ns_per_token": round(a_s * 1e9, 5), "beta_us": round(b_s * 1e6, 2), "r2": round(r2s, 5),
+                 "effective_GBps": round(per_token / a_s / 1e9, 1)},
+    }
+
+
 def make_runner(cfg):
     import workloads as wl
     return MlaRunner(cfg) if isinstance(cfg, wl.MLAConfig) else GqaRunner(cfg)
@@ -394,7 +495,8 @@ def main():
                     help="comma list of other workloads to report beside the headline ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["bench", "copy", "step", "append"], default="bench",
+    ap.add_argument("--no-latency-model", action="store_true", help="skip the t_A(T) calibration")
+    ap.add_argument("--mode", choices=["bench", "copy", "step", "append", "calibrate"], default="bench",
                     help="copy: time a plain device copy; step: run the headline step only; append: run the "
                          "workload's KV append only (both for profilers)")
     ap.add_argument("--copy-mb", type=int, default=1024)
@@ -413,6 +515,9 @@ def main():
     torch.cuda.set_device(0)
     if args.mode == "copy":
         copy_probe(args.copy_mb, args.steps)
+        return
+    if args.mode == "calibrate":
+        print(json.dumps({"mode": "calibrate", "latency_model": {k: calibrate_latency(k) for k in CALIB}}))
         return
 
     if args.workload in ROWS_WORKLOADS:
@@ -505,6 +610,10 @@ def main():
     if secondary:
         result["secondary"] = secondary
     result["kv_append"] = appends
+    if not args.no_latency_model:
+        del runner
+        torch.cuda.empty_cache()
+        result["latency_model"] = {k: calibrate_latency(k) for k in CALIB}
 
     if not args.no_cpu_baseline:
         import threadpoolctl
