@@ -158,8 +158,9 @@ int decode_attn_paged(const da_paged_desc* desc, const void* q, const void* kv_p
  * t <= seq_lens[b] - q_rows + i (causal among the new rows, older history
  * whole).  A row that sees no position (seq_lens[b] < q_rows - i) gets
  * out = 0 and lse = -inf.
- *   q_rows      1 .. 8, and q_rows * (Hq / Hkv) <= 8 (the kernels' largest
- *               head group); DA_ERR_UNSUPPORTED beyond.
+ *   q_rows      1 .. 16, with q_rows * (Hq / Hkv) <= 16 for bf16 queries
+ *               (groups of 8 to 16 (row, head) pairs run on the matrix cores)
+ *               and <= 8 for fp32; DA_ERR_UNSUPPORTED beyond.
  *   q           device, [B][q_rows][Hq][D] q_dtype.
  *   out         device, [B][q_rows][Hq][D] q_dtype (written).
  *   lse         device, fp32 [B][q_rows][Hq] (written), or NULL.

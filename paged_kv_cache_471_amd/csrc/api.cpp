@@ -13,6 +13,7 @@
 
 #include "../../include/decode_attn.h"
 #include "da_append.h"
+#include "da_gqa_mfma.h"
 #include "da_rows.h"
 
 namespace {
@@ -186,17 +187,26 @@ int check_paged(const da_paged_desc* d) {
     return DA_OK;
 }
 
-// (row, head) members of one KV head's group in the GQA kernel: q_rows times
+// Groups of 8 to 16 (row, head) members with bf16 queries run on the
+// matrix-core kernel (gqa_mfma.hip): at that many query heads per K/V page the
+// vector kernel is bound by its ALUs, not by HBM.
+bool gqa_uses_mfma(const da_paged_desc* d, int q_rows) {
+    const int want = q_rows * (d->num_q_heads / d->num_kv_heads);
+    return d->q_dtype == DA_BF16 && (d->kv_dtype == DA_BF16 || d->kv_dtype == DA_FP8_E4M3) && want >= 8 &&
+           want <= 16;
+}
+
+// (row, head) members of one KV head's group in the GQA kernels: q_rows times
 // the query heads per KV head, padded to a power of two; 0 when no kernel has
-// that many.
+// that many (16 on the matrix-core kernel, 8 on the vector one).
 int gqa_members(const da_paged_desc* d, int q_rows) {
     const int want = q_rows * (d->num_q_heads / d->num_kv_heads);
     int gs = 1;
     while (gs < want) gs <<= 1;
-    return gs <= 8 ? gs : 0;
+    return gs <= (gqa_uses_mfma(d, q_rows) ? 16 : 8) ? gs : 0;
 }
 
-int resolve_gqa_workers(const da_paged_desc* d, int members, int* G) {
+int resolve_gqa_workers(const da_paged_desc* d, int members, bool mfma, int* G) {
     if (d->workers > 0) {
         *G = d->workers;
         return DA_OK;
@@ -205,7 +215,8 @@ int resolve_gqa_workers(const da_paged_desc* d, int members, int* G) {
     int st = device_cus(&cus);
     if (st != DA_OK) return st;
     const int group_log2 = __builtin_ctz(static_cast<unsigned>(d->num_q_heads / d->num_kv_heads));
-    const int per_cu = da::gqa_workers_per_cu(d->q_dtype, d->kv_dtype, d->head_dim, members, group_log2);
+    const int per_cu = mfma ? da::gqa_mfma_workers_per_cu(d->kv_dtype, d->head_dim, group_log2)
+                            : da::gqa_workers_per_cu(d->q_dtype, d->kv_dtype, d->head_dim, members, group_log2);
     if (per_cu <= 0) return DA_ERR_UNSUPPORTED;
     int g = cus * per_cu;
     if (g > da::kMaxWorkers) g = da::kMaxWorkers;
@@ -247,14 +258,15 @@ int gqa_step(const da_paged_desc* d, int q_rows, const void* q, const void* kv_p
              const int32_t* seq_lens, float scale, void* out, float* lse, void* stream) {
     int st = check_paged(d);
     if (st != DA_OK) return st;
-    if (q_rows < 1 || q_rows > 8) return q_rows < 1 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
+    if (q_rows < 1 || q_rows > 16) return q_rows < 1 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
     const int members = gqa_members(d, q_rows);
     if (members == 0) return DA_ERR_UNSUPPORTED;
+    const bool mfma = gqa_uses_mfma(d, q_rows);
     if (q == nullptr || kv_pages == nullptr || page_table == nullptr || seq_lens == nullptr || out == nullptr)
         return DA_ERR_NULL;
     const int elem_kv = d->kv_dtype == DA_F32 ? 4 : (d->kv_dtype == DA_BF16 ? 2 : 1);
     const size_t lane_bytes = static_cast<size_t>(d->head_dim / 16) * elem_kv;
-    if (!aligned(kv_pages, lane_bytes < 16 ? lane_bytes : 16) || !aligned(q, 16) || !aligned(out, 16) ||
+    if (!aligned(kv_pages, lane_bytes < 16 && !mfma ? lane_bytes : 16) || !aligned(q, 16) || !aligned(out, 16) ||
         !aligned(lse, 4) || !aligned(page_table, 4) || !aligned(seq_lens, 4))
         return DA_ERR_SHAPE;
     if (!(scale == scale)) return DA_ERR_SHAPE;
@@ -262,7 +274,7 @@ int gqa_step(const da_paged_desc* d, int q_rows, const void* q, const void* kv_p
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     int G = 0;
-    st = resolve_gqa_workers(d, members, &G);
+    st = resolve_gqa_workers(d, members, mfma, &G);
     if (st != DA_OK) return st;
     const int group = d->num_q_heads / d->num_kv_heads;
     const int group_log2 = __builtin_ctz(static_cast<unsigned>(group));
@@ -293,7 +305,8 @@ int gqa_step(const da_paged_desc* d, int q_rows, const void* q, const void* kv_p
     ga.lse = lse;
     ga.o_part = sb.o_part;
     ga.lse_part = sb.lse_part;
-    hipError_t e = da::launch_gqa(d->q_dtype, d->kv_dtype, d->head_dim, members, ga, s, next_kernel_events());
+    hipError_t e = mfma ? da::launch_gqa_mfma(d->kv_dtype, d->head_dim, ga, s, next_kernel_events())
+                        : da::launch_gqa(d->q_dtype, d->kv_dtype, d->head_dim, members, ga, s, next_kernel_events());
     if (e != hipSuccess) return hip_fail(e);
 
     da::MergeArgs ma{};
@@ -604,7 +617,7 @@ int decode_attn_default_workers(const da_paged_desc* gqa, const da_mla_desc* mla
         if (st != DA_OK) return st;
         da_paged_desc dd = *gqa;
         dd.workers = 0;
-        st = resolve_gqa_workers(&dd, gqa_members(&dd, 1), &G);
+        st = resolve_gqa_workers(&dd, gqa_members(&dd, 1), gqa_uses_mfma(&dd, 1), &G);
     } else {
         st = check_mla(mla);
         if (st != DA_OK) return st;
