@@ -35,8 +35,10 @@ sys.path.insert(0, ROOT)
 METRIC = "decode-attention KV GB/s (% of HBM peak) + tokens/s per step, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK = 2.5e15         # dense bf16 FLOP/s, MI355X
-KERNEL_SOURCES = ["paged_kv_cache_471_amd/csrc/gqa.hip", "paged_kv_cache_471_amd/csrc/da_common.h",
-                  "paged_kv_cache_471_amd/csrc/da_launch.h", "paged_kv_cache_471_amd/csrc/da_plan.h"]
+# sources of the headline's dominant kernel (gqa_mfma_kernel: bf16, 4 query heads per KV head)
+KERNEL_SOURCES = ["paged_kv_cache_471_amd/csrc/gqa_mfma.hip", "paged_kv_cache_471_amd/csrc/da_gqa_mfma.h",
+                  "paged_kv_cache_471_amd/csrc/da_common.h", "paged_kv_cache_471_amd/csrc/da_launch.h",
+                  "paged_kv_cache_471_amd/csrc/da_plan.h"]
 PMC_FILE = os.path.join(ROOT, "profiles", "gqa_llama8b_pmc.md")
 
 
@@ -60,6 +62,14 @@ def traffic_from_profiles():
                 return None
             return d.get("traffic_bytes_per_launch")
     return None
+
+
+def gqa_kernel_name(cfg, rows: int = 1) -> str:
+    """The GQA attention kernel the library runs for this head shape."""
+    import workloads as wl
+    members = rows * cfg.q_heads // cfg.kv_heads
+    mfma = cfg.q_dtype == wl.BF16 and 4 <= members <= 16
+    return "gqa_mfma_kernel" if mfma else "gqa_attn_kernel"
 
 
 def workload_desc(cfg) -> str:
@@ -565,7 +575,7 @@ def main():
         "algorithmic_bytes_per_step": runner.bytes,
         "roofline": {
             "bound": "hbm",
-            "kernel": "mla_attn_kernel" if isinstance(cfg, wl.MLAConfig) else "gqa_attn_kernel",
+            "kernel": "mla_attn_kernel" if isinstance(cfg, wl.MLAConfig) else gqa_kernel_name(cfg),
             "achieved": round(kern_gbs, 2) if kern_gbs else None,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

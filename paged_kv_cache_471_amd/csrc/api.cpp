@@ -187,12 +187,14 @@ int check_paged(const da_paged_desc* d) {
     return DA_OK;
 }
 
-// Groups of 8 to 16 (row, head) members with bf16 queries run on the
-// matrix-core kernel (gqa_mfma.hip): at that many query heads per K/V page the
-// vector kernel is bound by its ALUs, not by HBM.
+// Groups of 4 to 16 (row, head) members with bf16 queries run on the
+// matrix-core kernel (gqa_mfma.hip): from 8 query heads per K/V page up the
+// vector kernel is bound by its ALUs, and at 4 the matrix-core kernel still
+// measured 2-3 % faster (less vector work beside the loads).  Smaller groups
+// and fp32 queries run on the vector kernel (gqa.hip).
 bool gqa_uses_mfma(const da_paged_desc* d, int q_rows) {
     const int want = q_rows * (d->num_q_heads / d->num_kv_heads);
-    return d->q_dtype == DA_BF16 && (d->kv_dtype == DA_BF16 || d->kv_dtype == DA_FP8_E4M3) && want >= 8 &&
+    return d->q_dtype == DA_BF16 && (d->kv_dtype == DA_BF16 || d->kv_dtype == DA_FP8_E4M3) && want >= 4 &&
            want <= 16;
 }
 
