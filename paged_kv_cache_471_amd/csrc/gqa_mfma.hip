@@ -131,10 +131,21 @@ __device__ __forceinline__ int k_dim(int s, int R) {
     else return 64 * (s >> 1) + 16 * R + 8 * (s & 1);
 }
 
+// Occupancy: fp8 is bounded to three workgroups (three waves per SIMD, at
+// most 168 registers each): its pages are small and the stream is bound by
+// latency (106.6 against 128.5 us on the long-context workload).  bf16 keeps
+// the compiler's own allocation (about 200 registers plus 32 accumulation
+// registers, two waves per SIMD); a tighter bound that allows three made it
+// 4-5 % slower.
+template <int KV>
+struct MOcc {
+    static constexpr int blocks_per_cu = KV == kFP8 ? 3 : 1;
+};
+
 // RG = log2(query heads per KV head).  Members m < 16 of a KV head's group are
 // (row m >> RG, head m & (2^RG - 1)); a.q_rows rows.
 template <int KV, int D, int RG>
-__global__ __launch_bounds__(kGqaBlock) void gqa_mfma_kernel(GqaArgs a) {
+__global__ __launch_bounds__(kGqaBlock, MOcc<KV>::blocks_per_cu) void gqa_mfma_kernel(GqaArgs a) {
     using C = MCfg<KV, D>;
     constexpr int KS = C::KS, KW = C::KW, DL = C::DL, VW = C::VW, EB = C::EB, NB = C::NB;
     constexpr int G = 1 << RG;
