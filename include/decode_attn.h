@@ -88,6 +88,12 @@ extern "C" {
  * (BF16, FP8_E4M3)}.  For fp8, k_scale and v_scale are device fp32
  * [num_kv_heads]; a stored code x of KV head j means e4m3(x) * scale[j].
  *
+ * Kernels: bf16 queries with 4 to 16 query heads (or, with several query
+ * rows, row x head pairs) per KV head run on the matrix cores (scores and
+ * values as MFMA products, softmax weights kept in fp32); fp32 queries and
+ * groups of 1 or 2 on the vector ALUs.  Both give the same semantics and the
+ * same tolerances; kv_pages must be 16-byte aligned on the matrix-core path.
+ *
  * workers: number of workers, 0 selects the library default (one per resident
  * wavefront).  A worker is one wavefront that processes one contiguous share
  * of all (request, KV head, page) units; see decode_attn_plan for the rule.
