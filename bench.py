@@ -12,8 +12,9 @@ KV cache are alternated so that consecutive steps cannot hit in the 256 MB
 last-level cache.
 
 Printed: one JSON line with the metric (algorithmic KV GB/s), tokens/s, the
-dominant kernel's roofline (its own duration from hipExtLaunchKernel events
-recorded over the timed region), HBM traffic from committed rocprofv3 counter
+dominant kernel's roofline (its own duration from hipExtLaunchKernel events,
+recorded over a second pass of the same number of steps, since the events
+lengthen the steps they bracket), HBM traffic from committed rocprofv3 counter
 runs when they match the current kernel source, the float64 CPU oracle's
 throughput on a bounded sample, the other workloads as secondary figures, and
 the paged KV append (this step's K/V or latent written into its page slot)
@@ -442,7 +443,12 @@ def time_runner(runner, steps, warmup, kernel_timer=True, warm_s=0.0):
     Settling (if warm_s > 0) steps the workload untimed for warm_s seconds
     first: the inputs were just generated on the host with the GPU idle, and a
     decode server steps back to back, so the timed steps should see the clock
-    the GPU settles at under this load, not its ramp from idle."""
+    the GPU settles at under this load, not its ramp from idle.
+
+    The timed steps run uninstrumented.  With kernel_timer, a second pass of
+    `steps` steps then launches the attention kernel with start/stop events
+    (hipExtLaunchKernelGGL) to read its own average duration; those events
+    lengthen a step by a few microseconds, so that pass is not the step time."""
     import torch
     import paged_kv_cache_471_amd as da
     if warm_s > 0:
@@ -453,9 +459,6 @@ def time_runner(runner, steps, warmup, kernel_timer=True, warm_s=0.0):
             torch.cuda.synchronize()
     for _ in range(warmup):
         runner.step()
-    torch.cuda.synchronize()
-    if kernel_timer:
-        da.timer_begin(steps)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -469,6 +472,10 @@ def time_runner(runner, steps, warmup, kernel_timer=True, warm_s=0.0):
     ms = start.elapsed_time(stop) / steps
     kms = None
     if kernel_timer:
+        da.timer_begin(steps)
+        for _ in range(steps):
+            runner.step()
+        torch.cuda.synchronize()
         tot, n = da.timer_end()
         kms = tot / n if n else None
     return ms, kms, wall

@@ -198,6 +198,12 @@ __device__ __forceinline__ float sum_xor32(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Two fp32 values -> packed bf16 pair (round to nearest even), one conversion.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2_t));
+}
+
 // Transposing 8-byte LDS read (gfx950): see the value-operand note in the kernel.
 __device__ __forceinline__ short4v ds_read_tr16(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p));
@@ -475,11 +481,18 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
                 // lane holds S^T[token tb*16 + 4 q4l + r][head hw + l16]
                 float sv[8];
                 float cmax = -__builtin_inff();
-                const int nv_lane = nvalid - 4 * q4l;           // live tokens counted from this lane's rows
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    sv[r] = r < nv_lane ? s0[r] * a.scale_log2 : -__builtin_inff();
-                    sv[4 + r] = 16 + r < nv_lane ? s1[r] * a.scale_log2 : -__builtin_inff();
+                    sv[r] = s0[r] * a.scale_log2;
+                    sv[4 + r] = s1[r] * a.scale_log2;
+                }
+                if (nvalid < kMlaChunk) {                       // wave-uniform: a history's last chunk
+                    const int nv_lane = nvalid - 4 * q4l;       // live tokens counted from this lane's rows
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (r >= nv_lane) sv[r] = -__builtin_inff();
+                        if (16 + r >= nv_lane) sv[4 + r] = -__builtin_inff();
+                    }
                 }
 #pragma unroll
                 for (int r = 0; r < 8; ++r) cmax = fmaxf(cmax, sv[r]);
@@ -495,7 +508,7 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
                         const float p0 = __builtin_amdgcn_exp2f(sv[4 * tb + r] - m_new);
                         const float p1 = __builtin_amdgcn_exp2f(sv[4 * tb + r + 1] - m_new);
                         psum += p0 + p1;
-                        pk[r >> 1] = f32_to_bf16_bits(p0) | (static_cast<uint32_t>(f32_to_bf16_bits(p1)) << 16);
+                        pk[r >> 1] = pack_bf16x2(p0, p1);
                     }
                     *reinterpret_cast<uint2*>(xa + pw_base + tb * 32) = make_uint2(pk[0], pk[1]);
                 }
