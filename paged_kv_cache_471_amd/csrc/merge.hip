@@ -28,6 +28,74 @@ namespace {
 constexpr int kThreads = 256;
 constexpr float kFloor = -3.0e38f;
 
+// NC float4 columns per thread (t, t + kThreads, ...; MLA's 512-value heads):
+// the pieces of all NC columns are loaded in one pass, so the partials cost
+// one round trip to memory rather than NC.  Same arithmetic and piece order
+// as the general path below.
+template <int NC>
+__device__ __forceinline__ void fold_columns(const MergeArgs& a, int t, int b, int j, int h0, int n, int gf,
+                                             int64_t start, int64_t W, int A, int heads, int gmask, int d4_log2) {
+    const int D = a.dim;
+    const int G = a.group;
+    int hh[NC], ccol[NC];
+    int64_t orow[NC];
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+        const int c = t + u * kThreads;
+        hh[u] = c >> d4_log2;
+        ccol[u] = c - (hh[u] << d4_log2);
+        const int slot_h = h0 + hh[u];
+        orow[u] = (static_cast<int64_t>(b) * a.rows + (slot_h >> a.group_log2)) * heads + (j << a.group_log2) +
+                  (slot_h & gmask);
+    }
+    float m[NC], z[NC];
+    float4 acc[NC];
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+        m[u] = -__builtin_inff();
+        z[u] = 0.0f;
+        acc[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+#pragma unroll 2
+    for (int i = 0; i < n; ++i) {
+        const int64_t sl = slot_of(gf + i, start, W, A);
+        float l[NC];
+        float4 o[NC];
+#pragma unroll
+        for (int u = 0; u < NC; ++u) {
+            l[u] = a.lse_part[sl * G + h0 + hh[u]];
+            o[u] = reinterpret_cast<const float4*>(a.o_part + (sl * G + h0) * D)[t + u * kThreads];
+        }
+#pragma unroll
+        for (int u = 0; u < NC; ++u) {
+            const float mn = fmaxf(fmaxf(m[u], l[u]), kFloor);
+            const float fo = __builtin_amdgcn_exp2f(m[u] - mn);   // 0 on the first piece
+            const float fn = __builtin_amdgcn_exp2f(l[u] - mn);
+            z[u] = z[u] * fo + fn;
+            acc[u].x = acc[u].x * fo + fn * o[u].x;
+            acc[u].y = acc[u].y * fo + fn * o[u].y;
+            acc[u].z = acc[u].z * fo + fn * o[u].z;
+            acc[u].w = acc[u].w * fo + fn * o[u].w;
+            m[u] = mn;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+        if (((h0 + hh[u]) >> a.group_log2) >= a.rows) continue;
+        const float inv = z[u] > 0.0f ? 1.0f / z[u] : 0.0f;
+        if (a.out_is_bf16) {
+            const uint32_t lo = f32_to_bf16_bits(acc[u].x * inv) | (static_cast<uint32_t>(f32_to_bf16_bits(acc[u].y * inv)) << 16);
+            const uint32_t hi = f32_to_bf16_bits(acc[u].z * inv) | (static_cast<uint32_t>(f32_to_bf16_bits(acc[u].w * inv)) << 16);
+            reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow[u] * D)[ccol[u]] = make_uint2(lo, hi);
+        } else {
+            reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow[u] * D)[ccol[u]] =
+                make_float4(acc[u].x * inv, acc[u].y * inv, acc[u].z * inv, acc[u].w * inv);
+        }
+        if (a.lse != nullptr && ccol[u] == 0)
+            a.lse[orow[u]] = z[u] > 0.0f ? (m[u] + __builtin_log2f(z[u])) * kLn2 : -__builtin_inff();
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     __shared__ float4 part[kThreads];
     __shared__ float pm[kThreads], pz[kThreads];
@@ -62,6 +130,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     const int heads = a.units << a.group_log2;            // query heads per row
     const int gmask = (1 << a.group_log2) - 1;
     const int d4_log2 = __builtin_ctz(static_cast<unsigned>(D)) - 2;   // D is a power of two
+    if (C4 == 2 * kThreads) {
+        fold_columns<2>(a, t, b, j, h0, n, gf, start, W, A, heads, gmask, d4_log2);
+        return;
+    }
     for (int c0 = 0; c0 < C4; c0 += cols) {
         const int c = c0 + t % cols;
         const int h = c >> d4_log2;
