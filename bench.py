@@ -18,7 +18,9 @@ lengthen the steps they bracket), HBM traffic from committed rocprofv3 counter
 runs when they match the current kernel source, the float64 CPU oracle's
 throughput on a bounded sample, the other workloads as secondary figures, and
 the paged KV append (this step's K/V or latent written into its page slot)
-timed on the headline, MLA and fp8 workloads.
+timed on the headline, MLA and fp8 workloads, the headline's per-call latency
+percentiles (each call between its own events, a separate pass), a 1 GiB
+device copy's bandwidth on the same GPU, and the device's properties.
 """
 from __future__ import annotations
 
@@ -481,6 +483,50 @@ def time_runner(runner, steps, warmup, kernel_timer=True, warm_s=0.0):
     return ms, kms, wall
 
 
+def step_percentiles(runner, calls):
+    """Per-call latency of `calls` steps, each bracketed by its own pair of
+    events (a separate pass after the timed steps): p10 / p50 / p90 in us."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record()
+        runner.step()
+        e1.record()
+    torch.cuda.synchronize()
+    us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+    pick = lambda f: round(us[min(len(us) - 1, int(f * len(us)))], 2)
+    return {"calls": calls, "p10_us": pick(0.10), "p50_us": pick(0.50), "p90_us": pick(0.90)}
+
+
+def copy_bandwidth(mb=1024, steps=20):
+    """Device-to-device copy of an mb-MiB fp32 buffer: bytes read plus written per second."""
+    import torch
+    n = mb * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n * 4 / (ms * 1e-3) / 1e9
+
+
+def device_info():
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "hbm_GiB": round(p.total_memory / 2 ** 30, 1)}
+
+
 def copy_probe(mb, steps):
     """Plain device copy of known size (reference for counter scaling and bandwidth)."""
     import torch
@@ -556,6 +602,7 @@ def main():
         return
 
     ms, kms, wall = time_runner(runner, args.steps, args.warmup, warm_s=SETTLE_S)
+    per_call = step_percentiles(runner, max(100, args.steps))
     headline_case = runner.case
     appends = {cfg.name: time_append(runner, args.steps, args.warmup, ms)}
     gbs = runner.bytes / (ms * 1e-3) / 1e9
@@ -627,9 +674,14 @@ def main():
     if secondary:
         result["secondary"] = secondary
     result["kv_append"] = appends
+    del runner
+    torch.cuda.empty_cache()
+    copy_gbs = copy_bandwidth()
+    result["step_latency"] = per_call
+    result["device"] = device_info()
+    result["copy_GBps"] = round(copy_gbs, 1)
+    result["pct_of_copy_GBps"] = round(100.0 * gbs / copy_gbs, 2)
     if not args.no_latency_model:
-        del runner
-        torch.cuda.empty_cache()
         result["latency_model"] = {k: calibrate_latency(k) for k in CALIB}
 
     if not args.no_cpu_baseline:
