@@ -140,6 +140,9 @@ __device__ __forceinline__ void cursor_next(Cursor& c, const int32_t* seq_lens, 
 // Written as inline assembly so that the compiler, which cannot tell which
 // LDS bytes such a load writes, does not drain every outstanding load before
 // each LDS access; completion is tracked with wait_vmcnt below instead.
+// m0 is listed as clobbered (the compiler warns that it is a reserved
+// register): on gfx950 LDS instructions do not read m0, and the built kernels
+// contain no m0 access other than these blocks' own writes.
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
