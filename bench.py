@@ -567,7 +567,8 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not offered "
-              "(the path shards by request, KV head or sequence; see DESIGN.md).", file=sys.stderr)
+              "(across GPUs the path would shard by request or by KV head with no exchange inside attention, "
+              "or by sequence with one exchange of partial outputs before the merge).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
