@@ -47,7 +47,8 @@
  *  - The library keeps one workspace per (device, stream), grown with
  *    hipMalloc the first time a shape needs more; growing synchronises the
  *    device.  Calls on one stream are ordered; calls on different streams
- *    use different workspaces.
+ *    use different workspaces.  The _ws entry points take a workspace the
+ *    caller owns instead and allocate nothing.
  */
 #ifndef DECODE_ATTN_H
 #define DECODE_ATTN_H
@@ -67,6 +68,7 @@ extern "C" {
 #define DA_ERR_UNSUPPORTED -4   /* valid request outside what the kernels implement */
 #define DA_ERR_WORKSPACE   -5   /* workspace could not be allocated */
 #define DA_ERR_HIP         -6   /* a HIP call failed; see decode_attn_last_hip_error() */
+#define DA_ERR_DATA        -7   /* decode_attn_validate_inputs: device data breaks a precondition */
 
 /* storage dtype tags */
 #define DA_F32       0          /* IEEE binary32 */
@@ -275,6 +277,51 @@ int decode_attn_plan(int32_t batch, const int32_t* seq_lens, int32_t page_size, 
  */
 int paged_kv_gather(const da_paged_desc* desc, int32_t mla, const void* kv_pages,
                     const int32_t* page_table, const int32_t* seq_lens, void* dense, void* stream);
+
+/*
+ * Caller-owned workspace (for callers that allocate up front: stream or graph
+ * capture, several streams sharing no library state).
+ *
+ * decode_attn_workspace_size: bytes of device workspace one call of the GQA
+ * path (gqa non-NULL) or the MLA path (mla non-NULL; exactly one of them)
+ * with q_rows query rows per request needs on the current device, for these
+ * descriptor values (batch, heads, dims, page size, max_pages_per_seq and
+ * workers; a workers value of 0 takes the device default).  Host query, no
+ * device work; 0 bytes for batch 0.  Returns the descriptor's own errors
+ * (DA_ERR_SHAPE / DA_ERR_DTYPE / DA_ERR_UNSUPPORTED) or DA_ERR_NULL.
+ *
+ * decode_attn_paged_ws / decode_attn_mla_ws: decode_attn_paged_rows /
+ * decode_attn_mla_rows (q_rows = 1 is the single-row call, bitwise the same
+ * result) with the workspace passed in: a device buffer of workspace_bytes,
+ * 256-byte aligned, owned by the caller and not kept by the library.  The
+ * library makes no allocation on this path.  Errors before any launch:
+ * DA_ERR_NULL (workspace NULL while batch > 0), DA_ERR_SHAPE (misaligned),
+ * DA_ERR_WORKSPACE (workspace_bytes below decode_attn_workspace_size), and
+ * those of the allocating entry points.  The workspace needs no initial
+ * value (each call writes what it later reads); it is in use until the call
+ * completes on `stream`, so calls that may overlap need distinct workspaces.
+ */
+int decode_attn_workspace_size(const da_paged_desc* gqa_or_null, const da_mla_desc* mla_or_null, int32_t q_rows,
+                               size_t* bytes);
+int decode_attn_paged_ws(const da_paged_desc* desc, int32_t q_rows, const void* q, const void* kv_pages,
+                         const int32_t* page_table, const int32_t* seq_lens, float scale, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream);
+int decode_attn_mla_ws(const da_mla_desc* desc, int32_t q_rows, const void* q, const void* kv_pages,
+                       const int32_t* page_table, const int32_t* seq_lens, float scale, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * decode_attn_validate_inputs - debug check of the data-dependent
+ * preconditions the kernels do not check: for every request b,
+ * 0 <= seq_lens[b] <= max_pages_per_seq * page_size, and every page-table
+ * entry the history uses (the first ceil(seq_lens[b] / page_size) of row b)
+ * lies in [0, num_pages).  Exactly one of gqa / mla is non-NULL and gives
+ * the sizes.  Copies seq_lens and page_table to the host and SYNCHRONISES
+ * `stream`; not for the hot path.  Returns DA_OK, DA_ERR_DATA on the first
+ * violation, or the descriptor / pointer errors.
+ */
+int decode_attn_validate_inputs(const da_paged_desc* gqa_or_null, const da_mla_desc* mla_or_null,
+                                const int32_t* page_table, const int32_t* seq_lens, void* stream);
 
 /* default number of workers for each path on the current device (host query). */
 int decode_attn_default_workers(const da_paged_desc* gqa_or_null, const da_mla_desc* mla_or_null,

@@ -19,12 +19,13 @@ LIB_PATH = os.path.join(_HERE, "libdecode_attn.so")
 
 DA_F32, DA_BF16, DA_FP8_E4M3 = 0, 1, 2
 STATUS = {0: "DA_OK", -1: "DA_ERR_NULL", -2: "DA_ERR_SHAPE", -3: "DA_ERR_DTYPE", -4: "DA_ERR_UNSUPPORTED",
-          -5: "DA_ERR_WORKSPACE", -6: "DA_ERR_HIP"}
+          -5: "DA_ERR_WORKSPACE", -6: "DA_ERR_HIP", -7: "DA_ERR_DATA"}
 
 EXPORTS = ("decode_attn_paged", "decode_attn_paged_rows", "decode_attn_mla", "decode_attn_mla_rows", "decode_attn_plan", "paged_kv_gather",
            "decode_kv_append", "decode_kv_append_mla",
            "decode_attn_default_workers", "decode_attn_status_str", "decode_attn_last_hip_error",
-           "decode_attn_timer_begin", "decode_attn_timer_end")
+           "decode_attn_timer_begin", "decode_attn_timer_end",
+           "decode_attn_workspace_size", "decode_attn_paged_ws", "decode_attn_mla_ws", "decode_attn_validate_inputs")
 
 
 class PagedDesc(ctypes.Structure):
@@ -82,6 +83,16 @@ def _load():
     lib.decode_attn_timer_begin.restype = ctypes.c_int
     lib.decode_attn_timer_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
     lib.decode_attn_timer_end.restype = ctypes.c_int
+    sz = ctypes.c_size_t
+    lib.decode_attn_workspace_size.argtypes = [ctypes.POINTER(PagedDesc), ctypes.POINTER(MLADesc), i32,
+                                               ctypes.POINTER(sz)]
+    lib.decode_attn_workspace_size.restype = ctypes.c_int
+    lib.decode_attn_paged_ws.argtypes = [ctypes.POINTER(PagedDesc), i32, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp]
+    lib.decode_attn_paged_ws.restype = ctypes.c_int
+    lib.decode_attn_mla_ws.argtypes = [ctypes.POINTER(MLADesc), i32, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp]
+    lib.decode_attn_mla_ws.restype = ctypes.c_int
+    lib.decode_attn_validate_inputs.argtypes = [ctypes.POINTER(PagedDesc), ctypes.POINTER(MLADesc), vp, vp, vp]
+    lib.decode_attn_validate_inputs.restype = ctypes.c_int
     return lib
 
 
@@ -311,6 +322,69 @@ def default_workers(q: torch.Tensor = None, kv_pages: torch.Tensor = None, page_
     return int(out.value)
 
 
+def _rows_view(q: torch.Tensor) -> torch.Tensor:
+    """[B][Hq][D] -> [B][1][Hq][D]; [B][n][Hq][D] as is."""
+    return q.unsqueeze(1) if q.dim() == 3 else q
+
+
+def workspace_size(desc, q_rows: int = 1) -> int:
+    """Device workspace bytes one call with this descriptor (PagedDesc or
+    MLADesc) and q_rows query rows needs (host query)."""
+    out = ctypes.c_size_t(0)
+    if isinstance(desc, MLADesc):
+        st = _lib.decode_attn_workspace_size(None, ctypes.byref(desc), int(q_rows), ctypes.byref(out))
+    else:
+        st = _lib.decode_attn_workspace_size(ctypes.byref(desc), None, int(q_rows), ctypes.byref(out))
+    _check(st, "decode_attn_workspace_size")
+    return int(out.value)
+
+
+def decode_attn_paged_ws(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                         scale: float, workspace: torch.Tensor, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                         *, k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                         workers: int = 0, stream=None):
+    """decode_attn_paged / decode_attn_paged_rows with a caller-owned workspace
+    (a byte tensor of at least workspace_size(...) bytes); q [B][Hq][D] or
+    [B][n][Hq][D], out shaped like q.  Allocates nothing."""
+    _need_cuda(q, kv_pages, page_table, seq_lens, k_scale, v_scale, workspace, out, lse)
+    q4 = _rows_view(q)
+    d = paged_desc(q4[:, 0], kv_pages, page_table, k_scale=k_scale, v_scale=v_scale, workers=workers)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = _lib.decode_attn_paged_ws(ctypes.byref(d), q4.shape[1], _ptr(q), _ptr(kv_pages), _ptr(page_table),
+                                   _ptr(seq_lens), float(scale), _ptr(out), _ptr(lse), _ptr(workspace), nbytes,
+                                   _stream(stream))
+    _check(st, "decode_attn_paged_ws")
+    return out, lse
+
+
+def decode_attn_mla_ws(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                       scale: float, workspace: torch.Tensor, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                       *, v_dim: int = 512, workers: int = 0, stream=None):
+    """decode_attn_mla / decode_attn_mla_rows with a caller-owned workspace;
+    q [B][H][576] or [B][n][H][576].  Allocates nothing."""
+    _need_cuda(q, kv_pages, page_table, seq_lens, workspace, out, lse)
+    q4 = _rows_view(q)
+    B, n, H, Dk = q4.shape
+    num_pages, P, _ = kv_pages.shape
+    d = MLADesc(B, H, Dk, v_dim, P, num_pages, page_table.shape[1], workers)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = _lib.decode_attn_mla_ws(ctypes.byref(d), n, _ptr(q), _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens),
+                                 float(scale), _ptr(out), _ptr(lse), _ptr(workspace), nbytes, _stream(stream))
+    _check(st, "decode_attn_mla_ws")
+    return out, lse
+
+
+def validate_inputs(desc, page_table: torch.Tensor, seq_lens: torch.Tensor, stream=None) -> int:
+    """Debug check of lengths and used page ids (synchronises); returns the
+    status (0, or -7 = DA_ERR_DATA when a precondition fails)."""
+    _need_cuda(page_table, seq_lens)
+    if isinstance(desc, MLADesc):
+        return _lib.decode_attn_validate_inputs(None, ctypes.byref(desc), _ptr(page_table), _ptr(seq_lens),
+                                                _stream(stream))
+    return _lib.decode_attn_validate_inputs(ctypes.byref(desc), None, _ptr(page_table), _ptr(seq_lens),
+                                            _stream(stream))
+
+
 def timer_begin(max_launches: int):
     """Time the main attention kernel of each following call (see decode_attn.h)."""
     _check(_lib.decode_attn_timer_begin(int(max_launches)), "decode_attn_timer_begin")
@@ -326,4 +400,5 @@ def timer_end():
 
 __all__ = ["timer_begin", "timer_end", "decode_attn_paged", "decode_attn_paged_rows", "decode_attn_mla",
            "decode_attn_mla_rows", "decode_attn_plan", "paged_kv_gather", "default_workers",
-           "PagedDesc", "MLADesc", "DecodeAttnError", "LIB_PATH", "EXPORTS", "lib", "decode_kv_append", "decode_kv_append_mla"]
+           "PagedDesc", "MLADesc", "DecodeAttnError", "LIB_PATH", "EXPORTS", "lib", "decode_kv_append", "decode_kv_append_mla",
+           "workspace_size", "decode_attn_paged_ws", "decode_attn_mla_ws", "validate_inputs"]

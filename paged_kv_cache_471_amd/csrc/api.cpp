@@ -99,11 +99,26 @@ size_t split_layout(int streams, int G, int heads, int dim, char* base, SplitBuf
     return off;
 }
 
+// A workspace the caller owns (the _ws entry points): used as given, never
+// grown; the library allocates nothing on that path.
+struct CallerWorkspace {
+    void* ptr;
+    size_t bytes;
+};
+
 int get_split_buffers(hipStream_t s, int streams, int G, int heads, int dim, SplitBuffers* sb,
-                      size_t extra_ints = 0) {
+                      size_t extra_ints = 0, const CallerWorkspace* cws = nullptr) {
+    const size_t need = split_layout(streams, G, heads, dim, nullptr, nullptr, extra_ints);
     void* base = nullptr;
-    int st = get_workspace(s, split_layout(streams, G, heads, dim, nullptr, nullptr, extra_ints), &base);
-    if (st != DA_OK) return st;
+    if (cws != nullptr) {
+        if (cws->ptr == nullptr) return DA_ERR_NULL;
+        if (!aligned(cws->ptr, 256)) return DA_ERR_SHAPE;
+        if (cws->bytes < need) return DA_ERR_WORKSPACE;
+        base = cws->ptr;
+    } else {
+        int st = get_workspace(s, need, &base);
+        if (st != DA_OK) return st;
+    }
     split_layout(streams, G, heads, dim, static_cast<char*>(base), sb, extra_ints);
     return DA_OK;
 }
@@ -256,8 +271,44 @@ int resolve_mla_workers(const da_mla_desc* d, int* G) {
     return DA_OK;
 }
 
+// Workspace bytes of one call: the same checks, worker count and layout as
+// gqa_step / mla_step, so that a buffer of this size is always enough.
+int gqa_workspace_bytes(const da_paged_desc* d, int q_rows, size_t* bytes) {
+    int st = check_paged(d);
+    if (st != DA_OK) return st;
+    if (q_rows < 1 || q_rows > 16) return q_rows < 1 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
+    const int members = gqa_members(d, q_rows);
+    if (members == 0) return DA_ERR_UNSUPPORTED;
+    *bytes = 0;
+    if (d->batch == 0) return DA_OK;
+    int G = 0;
+    st = resolve_gqa_workers(d, members, gqa_uses_mfma(d, q_rows), &G);
+    if (st != DA_OK) return st;
+    *bytes = split_layout(d->batch * d->num_kv_heads, G, members, d->head_dim, nullptr, nullptr, 0);
+    return DA_OK;
+}
+
+int mla_workspace_bytes(const da_mla_desc* dd, int q_rows, size_t* bytes) {
+    int st = check_mla(dd);
+    if (st != DA_OK) return st;
+    if (q_rows < 1) return DA_ERR_SHAPE;
+    da_mla_desc rd = *dd;
+    rd.batch = dd->batch * q_rows;
+    if (rd.batch > da::kMaxBatch) return DA_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(rd.batch) * rd.max_pages_per_seq >= (int64_t(1) << 31)) return DA_ERR_UNSUPPORTED;
+    *bytes = 0;
+    if (rd.batch == 0) return DA_OK;
+    int G = 0;
+    st = resolve_mla_workers(&rd, &G);
+    if (st != DA_OK) return st;
+    const size_t extra = q_rows > 1 ? static_cast<size_t>(rd.batch) * (1 + rd.max_pages_per_seq) : 0;
+    *bytes = split_layout(rd.batch, G, rd.num_heads, rd.v_dim, nullptr, nullptr, extra);
+    return DA_OK;
+}
+
 int gqa_step(const da_paged_desc* d, int q_rows, const void* q, const void* kv_pages, const int32_t* page_table,
-             const int32_t* seq_lens, float scale, void* out, float* lse, void* stream) {
+             const int32_t* seq_lens, float scale, void* out, float* lse, void* stream,
+             const CallerWorkspace* cws = nullptr) {
     int st = check_paged(d);
     if (st != DA_OK) return st;
     if (q_rows < 1 || q_rows > 16) return q_rows < 1 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
@@ -282,7 +333,7 @@ int gqa_step(const da_paged_desc* d, int q_rows, const void* q, const void* kv_p
     const int group_log2 = __builtin_ctz(static_cast<unsigned>(group));
     const int streams = d->batch * d->num_kv_heads;
     SplitBuffers sb;
-    st = get_split_buffers(s, streams, G, members, d->head_dim, &sb);
+    st = get_split_buffers(s, streams, G, members, d->head_dim, &sb, 0, cws);
     if (st != DA_OK) return st;
 
     da::GqaArgs ga{};
@@ -341,7 +392,8 @@ int gqa_step(const da_paged_desc* d, int q_rows, const void* q, const void* kv_p
 // the workspace); q, out and lse [batch][q_rows][heads][...] are already laid
 // out as those requests.
 int mla_step(const da_mla_desc* dd, int q_rows, const void* q, const void* kv_pages, const int32_t* page_table,
-             const int32_t* seq_lens, float scale, void* out, float* lse, void* stream) {
+             const int32_t* seq_lens, float scale, void* out, float* lse, void* stream,
+             const CallerWorkspace* cws = nullptr) {
     int st = check_mla(dd);
     if (st != DA_OK) return st;
     if (q_rows < 1) return DA_ERR_SHAPE;
@@ -364,7 +416,7 @@ int mla_step(const da_mla_desc* dd, int q_rows, const void* q, const void* kv_pa
     if (st != DA_OK) return st;
     SplitBuffers sb;
     const size_t extra = q_rows > 1 ? static_cast<size_t>(d->batch) * (1 + d->max_pages_per_seq) : 0;
-    st = get_split_buffers(s, d->batch, G, d->num_heads, d->v_dim, &sb, extra);
+    st = get_split_buffers(s, d->batch, G, d->num_heads, d->v_dim, &sb, extra, cws);
     if (st != DA_OK) return st;
     if (q_rows > 1) {
         da::RowsArgs ra{};
@@ -438,6 +490,7 @@ const char* decode_attn_status_str(int status) {
         case DA_ERR_UNSUPPORTED: return "valid request outside what the kernels implement";
         case DA_ERR_WORKSPACE: return "workspace allocation failed";
         case DA_ERR_HIP: return "a HIP call failed";
+        case DA_ERR_DATA: return "device data violates a precondition (length or page id out of range)";
         default: return "unknown status";
     }
 }
@@ -503,6 +556,55 @@ int decode_attn_mla_rows(const da_mla_desc* d, int32_t q_rows, const void* q, co
                          const int32_t* page_table, const int32_t* seq_lens, float scale, void* out, float* lse,
                          void* stream) {
     return mla_step(d, q_rows, q, kv_pages, page_table, seq_lens, scale, out, lse, stream);
+}
+
+int decode_attn_workspace_size(const da_paged_desc* gqa, const da_mla_desc* mla, int32_t q_rows, size_t* bytes) {
+    if (bytes == nullptr || (gqa == nullptr) == (mla == nullptr)) return DA_ERR_NULL;
+    return gqa != nullptr ? gqa_workspace_bytes(gqa, q_rows, bytes) : mla_workspace_bytes(mla, q_rows, bytes);
+}
+
+int decode_attn_paged_ws(const da_paged_desc* d, int32_t q_rows, const void* q, const void* kv_pages,
+                         const int32_t* page_table, const int32_t* seq_lens, float scale, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    const CallerWorkspace cws{workspace, workspace_bytes};
+    return gqa_step(d, q_rows, q, kv_pages, page_table, seq_lens, scale, out, lse, stream, &cws);
+}
+
+int decode_attn_mla_ws(const da_mla_desc* d, int32_t q_rows, const void* q, const void* kv_pages,
+                       const int32_t* page_table, const int32_t* seq_lens, float scale, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    const CallerWorkspace cws{workspace, workspace_bytes};
+    return mla_step(d, q_rows, q, kv_pages, page_table, seq_lens, scale, out, lse, stream, &cws);
+}
+
+int decode_attn_validate_inputs(const da_paged_desc* gqa, const da_mla_desc* mla, const int32_t* page_table,
+                                const int32_t* seq_lens, void* stream) {
+    if ((gqa == nullptr) == (mla == nullptr) || page_table == nullptr || seq_lens == nullptr) return DA_ERR_NULL;
+    int st = gqa != nullptr ? check_paged(gqa) : check_mla(mla);
+    if (st != DA_OK) return st;
+    const int B = gqa != nullptr ? gqa->batch : mla->batch;
+    const int P = gqa != nullptr ? gqa->page_size : mla->page_size;
+    const int max_pages = gqa != nullptr ? gqa->max_pages_per_seq : mla->max_pages_per_seq;
+    const int num_pages = gqa != nullptr ? gqa->num_pages : mla->num_pages;
+    if (B == 0) return DA_OK;
+    std::vector<int32_t> lens(static_cast<size_t>(B));
+    std::vector<int32_t> table(static_cast<size_t>(B) * max_pages);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(lens.data(), seq_lens, lens.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(table.data(), page_table, table.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e);
+    for (int b = 0; b < B; ++b) {
+        const int64_t L = lens[static_cast<size_t>(b)];
+        if (L < 0 || L > static_cast<int64_t>(max_pages) * P) return DA_ERR_DATA;
+        const int64_t used = (L + P - 1) / P;
+        for (int64_t p = 0; p < used; ++p) {
+            const int32_t id = table[static_cast<size_t>(b) * max_pages + p];
+            if (id < 0 || id >= num_pages) return DA_ERR_DATA;
+        }
+    }
+    return DA_OK;
 }
 
 int decode_kv_append(const da_paged_desc* d, const void* k_new, const void* v_new, void* kv_pages,

@@ -175,3 +175,61 @@ def test_mla_rows_rejected_before_any_device_call(lib):
                              (dict(num_heads=96), 2, -4)]:
         d = lib.MLADesc(**{**good, **kw})
         assert f(ctypes.byref(d), rows, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, None) == status
+
+
+# ---- caller-owned workspace and the input validator: host-side checks
+
+def test_workspace_size_host_checks(lib):
+    L = lib.lib()
+    out = ctypes.c_size_t(123)
+    d, m = _desc(lib, workers=64), _mla_desc(lib, workers=32)
+    assert L.decode_attn_workspace_size(ctypes.byref(d), None, 1, None) == -1
+    assert L.decode_attn_workspace_size(ctypes.byref(d), ctypes.byref(m), 1, ctypes.byref(out)) == -1
+    assert L.decode_attn_workspace_size(None, None, 1, ctypes.byref(out)) == -1
+    assert L.decode_attn_workspace_size(ctypes.byref(d), None, 0, ctypes.byref(out)) == -2
+    assert L.decode_attn_workspace_size(ctypes.byref(_desc(lib, head_dim=96)), None, 1, ctypes.byref(out)) == -4
+    assert L.decode_attn_workspace_size(None, ctypes.byref(_mla_desc(lib, num_heads=48)), 1, ctypes.byref(out)) == -4
+    # with a forced worker count the size is a host computation (no device query)
+    sizes = []
+    for workers in (16, 64, 256):
+        assert L.decode_attn_workspace_size(ctypes.byref(_desc(lib, workers=workers)), None, 1,
+                                            ctypes.byref(out)) == 0
+        sizes.append(out.value)
+    assert 0 < sizes[0] < sizes[1] < sizes[2]          # partial slots grow with the workers
+    assert L.decode_attn_workspace_size(ctypes.byref(_desc(lib, workers=64, batch=0)), None, 1,
+                                        ctypes.byref(out)) == 0 and out.value == 0
+    one, two = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert L.decode_attn_workspace_size(None, ctypes.byref(m), 1, ctypes.byref(one)) == 0
+    assert L.decode_attn_workspace_size(None, ctypes.byref(m), 2, ctypes.byref(two)) == 0
+    assert two.value > one.value > 0                  # two rows: twice the requests plus their page tables
+
+
+def test_ws_entry_points_reject_before_any_device_call(lib):
+    L = lib.lib()
+    d, m = _desc(lib, workers=64), _mla_desc(lib, workers=32)
+    need, mneed = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert L.decode_attn_workspace_size(ctypes.byref(d), None, 1, ctypes.byref(need)) == 0
+    assert L.decode_attn_workspace_size(None, ctypes.byref(m), 1, ctypes.byref(mneed)) == 0
+    WS = 0x200000                                     # 256-byte aligned, never dereferenced
+    args = (FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE)
+    assert L.decode_attn_paged_ws(ctypes.byref(d), 1, *args, WS, need.value - 1, None) == -5
+    assert L.decode_attn_paged_ws(ctypes.byref(d), 1, *args, None, need.value, None) == -1
+    assert L.decode_attn_paged_ws(ctypes.byref(d), 1, *args, WS + 16, need.value, None) == -2
+    assert L.decode_attn_paged_ws(ctypes.byref(_desc(lib, head_dim=96)), 1, *args, WS, need.value, None) == -4
+    assert L.decode_attn_paged_ws(ctypes.byref(d), 0, *args, WS, need.value, None) == -2
+    assert L.decode_attn_mla_ws(ctypes.byref(m), 1, *args, WS, mneed.value - 1, None) == -5
+    assert L.decode_attn_mla_ws(ctypes.byref(m), 1, *args, None, mneed.value, None) == -1
+    assert L.decode_attn_mla_ws(ctypes.byref(_mla_desc(lib, page_size=16)), 1, *args, WS, mneed.value, None) == -4
+    # batch 0: nothing to do, no workspace needed
+    assert L.decode_attn_paged_ws(ctypes.byref(_desc(lib, batch=0)), 1, *args, None, 0, None) == 0
+
+
+def test_validate_inputs_host_checks(lib):
+    L = lib.lib()
+    d, m = _desc(lib), _mla_desc(lib)
+    assert L.decode_attn_validate_inputs(None, None, FAKE, FAKE, None) == -1
+    assert L.decode_attn_validate_inputs(ctypes.byref(d), ctypes.byref(m), FAKE, FAKE, None) == -1
+    assert L.decode_attn_validate_inputs(ctypes.byref(d), None, None, FAKE, None) == -1
+    assert L.decode_attn_validate_inputs(ctypes.byref(_desc(lib, num_pages=0)), None, FAKE, FAKE, None) == -2
+    assert L.decode_attn_validate_inputs(None, ctypes.byref(_mla_desc(lib, batch=0)), FAKE, FAKE, None) == 0
+    assert L.decode_attn_status_str(-7)
