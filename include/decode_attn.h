@@ -85,7 +85,8 @@ extern "C" {
  * lse: [batch][num_q_heads] fp32.  page_table: int32 [batch][max_pages_per_seq].
  * seq_lens: int32 [batch].
  *
- * Offered: head_dim in {64, 128}; page_size 16; num_q_heads / num_kv_heads in
+ * Offered: head_dim in {64, 128}; page_size 16, 32, 64, 128 or 256 (the
+ * kernels walk 16-token tiles of a page); num_q_heads / num_kv_heads in
  * {1, 2, 4, 8}; (q_dtype, kv_dtype) in {(F32, F32), (BF16, BF16),
  * (BF16, FP8_E4M3)}.  For fp8, k_scale and v_scale are device fp32
  * [num_kv_heads]; a stored code x of KV head j means e4m3(x) * scale[j].

@@ -192,10 +192,13 @@ int check_paged(const da_paged_desc* d) {
     if (!combo) return DA_ERR_DTYPE;
     const int group = d->num_q_heads / d->num_kv_heads;
     if (d->head_dim != 64 && d->head_dim != 128) return DA_ERR_UNSUPPORTED;
-    if (d->page_size != 16) return DA_ERR_UNSUPPORTED;
+    // pages of 16 << k tokens: the kernels walk 16-token tiles
+    if (d->page_size < 16 || d->page_size > 256 || (d->page_size & (d->page_size - 1)) != 0)
+        return DA_ERR_UNSUPPORTED;
     if (group != 1 && group != 2 && group != 4 && group != 8) return DA_ERR_UNSUPPORTED;
     if (d->batch > da::kMaxBatch || d->workers > da::kMaxWorkers) return DA_ERR_UNSUPPORTED;
-    const int64_t units_bound = static_cast<int64_t>(d->num_kv_heads) * d->batch * d->max_pages_per_seq;
+    const int64_t units_bound =
+        static_cast<int64_t>(d->num_kv_heads) * d->batch * d->max_pages_per_seq * (d->page_size / 16);
     if (units_bound >= (int64_t(1) << 31)) return DA_ERR_UNSUPPORTED;
     if (static_cast<int64_t>(d->max_pages_per_seq) * d->page_size >= (int64_t(1) << 31)) return DA_ERR_SHAPE;
     if (d->kv_dtype == DA_FP8_E4M3 && (d->k_scale == nullptr || d->v_scale == nullptr)) return DA_ERR_NULL;
@@ -348,6 +351,7 @@ int gqa_step(const da_paged_desc* d, int q_rows, const void* q, const void* kv_p
     ga.q_heads = d->num_q_heads;
     ga.kv_heads = d->num_kv_heads;
     ga.page_size = d->page_size;
+    ga.tile_shift = __builtin_ctz(static_cast<unsigned>(d->page_size)) - 4;
     ga.max_pages = d->max_pages_per_seq;
     ga.workers = G;
     ga.q_rows = q_rows;

@@ -31,6 +31,11 @@ struct GqaArgs {
     const float* v_scale;
     float scale_log2;       // softmax scale * log2(e)
     int batch, q_heads, kv_heads, page_size, max_pages, workers;
+    // The kernels work in tiles of 16 tokens; a page holds 2^tile_shift of
+    // them (page_size = 16 << tile_shift), so tile t of a history lies in
+    // page-table entry t >> tile_shift, from token 16 (t mod 2^tile_shift)
+    // of that page.
+    int tile_shift;
     // Query rows per request (q, out [batch][q_rows][q_heads][head_dim]): row i
     // sees history positions t <= len - q_rows + i.  The kernel's head group
     // GS holds the q_rows x (q_heads / kv_heads) (row, head) pairs of one KV

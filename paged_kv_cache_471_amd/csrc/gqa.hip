@@ -167,7 +167,8 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
     const int64_t c0 = sh.c0;
     const int n = static_cast<int>(sh.c1 - sh.c0);
     const char* kvb = static_cast<const char*>(a.kv);
-    const int64_t block_elems = static_cast<int64_t>(kPage) * D;   // one (page, K|V, head) block
+    const int64_t block_elems = static_cast<int64_t>(a.page_size) * D;   // one (page, K|V, head) block
+    const int tile_mask = (1 << a.tile_shift) - 1;
     const int lane_off = (row * D + col * DL) * EB;                  // bytes within a 4-row group
 
     Cursor cc;                                 // compute cursor
@@ -181,10 +182,12 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
     // first use, one unit later, so its latency hides behind a page of work.
     const cint32_t* page_table = (const cint32_t*)a.page_table;
     auto page_id = [&](const Cursor& c) -> int {
-        return page_table[static_cast<int64_t>(c.b) * a.max_pages + c.p];
+        return page_table[static_cast<int64_t>(c.b) * a.max_pages + (c.p >> a.tile_shift)];
     };
+    // the tile issued is always the load cursor's
     auto issue = [&](PageBuf<NW>& buf, int pid, int j) {
-        const char* kbase = kvb + (gqa_kv_offset(pid, 0, j, 0, Hkv, kPage, D)) * EB + lane_off;
+        const int slot0 = (lc.p & tile_mask) * kPage;          // first token of the tile in its page
+        const char* kbase = kvb + (gqa_kv_offset(pid, 0, j, slot0, Hkv, a.page_size, D)) * EB + lane_off;
         const char* vbase = kbase + static_cast<int64_t>(Hkv) * block_elems * EB;
 #pragma unroll
         for (int i = 0; i < kTPL; ++i) load_words<NW>(buf.k[i], kbase + i * 4 * D * EB);

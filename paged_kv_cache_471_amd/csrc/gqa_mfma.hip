@@ -177,7 +177,8 @@ __global__ __launch_bounds__(kGqaBlock, MOcc<KV>::blocks_per_cu) void gqa_mfma_k
     const int64_t c0 = sh.c0;
     const int n = static_cast<int>(sh.c1 - sh.c0);
     const char* kvb = static_cast<const char*>(a.kv);
-    const int64_t block_bytes = static_cast<int64_t>(kPage) * D * EB;    // one (page, K|V, head) block
+    const int64_t block_bytes = static_cast<int64_t>(a.page_size) * D * EB;   // one (page, K|V, head) block
+    const int tile_mask = (1 << a.tile_shift) - 1;
 
     // member of this lane's score column, and its row / query head offset
     const int mrow = Cc >> RG;                       // query row of member Cc
@@ -191,12 +192,14 @@ __global__ __launch_bounds__(kGqaBlock, MOcc<KV>::blocks_per_cu) void gqa_mfma_k
 
     const cint32_t* page_table = (const cint32_t*)a.page_table;
     auto page_id = [&](const Cursor& c) -> int {
-        return page_table[static_cast<int64_t>(c.b) * a.max_pages + c.p];
+        return page_table[static_cast<int64_t>(c.b) * a.max_pages + (c.p >> a.tile_shift)];
     };
     const int k_lane = Cc * D * EB + 16 * R;                 // byte of piece 0 in the K block
     const int v_lane = 4 * R * D * EB + Cc * DL * EB;        // byte of token 4R, dim C DL in the V block
+    // the tile issued is always the load cursor's
     auto issue = [&](MPage<KV, D>& buf, int pid, int j) {
-        const char* kbase = kvb + gqa_kv_offset(pid, 0, j, 0, Hkv, kPage, D) * EB;
+        const int slot0 = (lc.p & tile_mask) * kPage;          // first token of the tile in its page
+        const char* kbase = kvb + gqa_kv_offset(pid, 0, j, slot0, Hkv, a.page_size, D) * EB;
         const char* vbase = kbase + static_cast<int64_t>(Hkv) * block_bytes;
         if constexpr (KW == 4) {
             load_nt<4>(buf.k, kbase + k_lane);

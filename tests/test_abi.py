@@ -50,7 +50,9 @@ FAKE = 0x10000   # never dereferenced: every case below fails validation first
 @pytest.mark.parametrize("kw,status", [
     (dict(num_q_heads=6, num_kv_heads=4), -2),        # Hq % Hkv != 0
     (dict(head_dim=96), -4),                          # unsupported head_dim
-    (dict(page_size=32), -4),                         # unsupported page size
+    (dict(page_size=24), -4),                         # unsupported page sizes
+    (dict(page_size=8), -4),
+    (dict(page_size=512), -4),
     (dict(q_dtype=7), -3),                            # unknown dtype
     (dict(q_dtype=0, kv_dtype=1), -3),                # combination not offered
     (dict(q_dtype=1, kv_dtype=2), -1),                # fp8 without scales

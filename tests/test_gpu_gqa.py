@@ -234,3 +234,27 @@ def test_fp8_long_context_reduced_whole():
     out, lse, _ = run(case)
     ro, rl = gqa_oracle(case)
     assert_close_gqa(case, out, lse, ro, rl, label="longfp8 8k")
+
+
+# ----------------------------------------------------------------------------- page sizes above 16
+
+@pytest.mark.parametrize("P", [32, 64, 256])
+@pytest.mark.parametrize("qd,kd", DTYPES)
+@pytest.mark.parametrize("Hq,Hkv,D", [(8, 2, 128), (32, 8, 128), (16, 2, 64)])
+def test_page_sizes(P, qd, kd, Hq, Hkv, D):
+    """Pages of P = 16 << k tokens: the kernels walk 16-token tiles of each page."""
+    cfg = wl.GQAConfig("t", 9, 6, Hq, Hkv, D, P, qd, kd, "uniform:1:1500")
+    case = wl.make_gqa_case(cfg, poison=True, extra_pages=2, seed=500 + P + Hq + D + kd)
+    ro, rl = gqa_oracle(case)
+    for workers in (0, 333):
+        out, lse, _ = run(case, workers=workers)
+        assert_close_gqa(case, out, lse, ro, rl, label=f"P{P} {qd}/{kd} {Hq}/{Hkv} D{D} G={workers}")
+
+
+@pytest.mark.parametrize("lens", [[1], [15, 16, 17], [63, 64, 65], [64 * 5 + 31, 0, 2], [1000]])
+def test_page_size_64_edge_lengths(lens):
+    cfg = wl.GQAConfig("t", 9, len(lens), 32, 8, 128, 64, wl.BF16, wl.BF16, "fixed:1")
+    case = wl.make_gqa_case(cfg, seq_lens=np.array(lens, dtype=np.int32), poison=True, extra_pages=1, seed=6)
+    out, lse, _ = run(case)
+    ro, rl = gqa_oracle(case)
+    assert_close_gqa(case, out, lse, ro, rl, label=f"P64 lens {lens}")

@@ -1,7 +1,7 @@
 """Seeded random sweep of the decode-attention entry points against the oracle.
 
 Each case draws its shape from a seeded generator: dtype pair, head_dim, query
-and KV head counts, query rows per request, batch, a length mix (short,
+and KV head counts, query rows per request, batch, page size, a length mix (short,
 page-boundary and long histories, empty requests), the worker count (default
 or forced, so that streams split at arbitrary pages) and the softmax scale
 (the default or eight times it).  The multi-row entry points are called; a
@@ -87,8 +87,9 @@ def test_gqa_random(seed):
     q_dtype, kv_dtype = GQA_DTYPES[seed % 3]
     Hq, Hkv, D, n = _gqa_shape(rng, q_dtype)
     B = int(rng.integers(1, 24))
-    lens = _lengths(rng, B, 16)
-    cfg = wl.GQAConfig("sweep", 50 + seed, B, Hq, Hkv, D, 16, q_dtype, kv_dtype, "fixed:1")
+    P = int(rng.choice([16, 16, 32, 64, 128]))
+    lens = _lengths(rng, B, P)
+    cfg = wl.GQAConfig("sweep", 50 + seed, B, Hq, Hkv, D, P, q_dtype, kv_dtype, "fixed:1")
     sharp = bool(rng.integers(0, 2))
     case = wl.make_gqa_case(cfg, seq_lens=lens, poison=True, extra_pages=2, seed=9000 + seed,
                             scale=(8.0 if sharp else 1.0) / np.sqrt(D))
@@ -96,14 +97,14 @@ def test_gqa_random(seed):
     q32 = rng.standard_normal((B, n, Hq, D)).astype(np.float32)
     q = q32 if q_dtype == F32 else wl.to_bf16_bits(q32)
     ro, rl = oracle.paged_decode_attention_rows(q, q_dtype, case.kv, kv_dtype, case.page_table, case.seq_lens,
-                                                16, case.scale, case.k_scale, case.v_scale)
+                                                P, case.scale, case.k_scale, case.v_scale)
     dev = lambda x: None if x is None else torch.from_numpy(x).cuda()
     qd = to_dev_storage(q, q_dtype)
     kv = to_dev_storage(case.kv, kv_dtype)
     pt, sl, ks, vs = dev(case.page_table), dev(case.seq_lens), dev(case.k_scale), dev(case.v_scale)
     out, lse = da.decode_attn_paged_rows(qd, kv, pt, sl, case.scale, k_scale=ks, v_scale=vs, workers=workers)
     torch.cuda.synchronize()
-    label = f"seed {seed}: q{q_dtype}/kv{kv_dtype} {Hq}/{Hkv} D{D} rows {n} B{B} G={workers} sharp={sharp}"
+    label = f"seed {seed}: q{q_dtype}/kv{kv_dtype} {Hq}/{Hkv} D{D} P{P} rows {n} B{B} G={workers} sharp={sharp}"
     _check(out, lse, ro, rl, kv_dtype, label)
     if n == 1:
         out1, lse1 = da.decode_attn_paged(qd[:, 0].contiguous(), kv, pt, sl, case.scale, k_scale=ks, v_scale=vs,
