@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
         const int64_t out_row = (static_cast<int64_t>(b) * a.rows + r) * heads + (j << a.group_log2) + (slot_h & gmask);
         float m = -__builtin_inff(), z = 0.0f;
         float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-#pragma unroll 4
+#pragma unroll 8
         for (int i = q; i < n; i += PL) {
             const int64_t sl = slot_of(gf + i, start, W, A);
             const float l = a.lse_part[sl * G + h0 + h];
