@@ -245,7 +245,10 @@ int decode_kv_append_mla(const da_mla_desc* desc, const void* latent_new, void* 
  * decode_attn_plan - run the split-KV planner that the attention kernels
  * execute in-kernel, alone, and write what it decides (for tests and tools).
  * The rule: stream (b, j), j < units, owns ceil(seq_lens[b] / page_size) page
- * units; streams are ordered b-major; W is the total; A = min(workers, W)
+ * units (the GQA kernels plan in 16-token tiles whatever their cache's page
+ * size, with units = num_kv_heads: pass page_size 16 to reproduce their
+ * plan; the MLA kernel plans in its pages, with units = 1); streams are
+ * ordered b-major; W is the total; A = min(workers, W)
  * workers are active and worker g < A takes units [floor(g*W/A),
  * floor((g+1)*W/A)).  The step ends with its slowest worker, so the largest
  * share is what the rule minimises ("Analytical Provisioning for Attention-FFN
