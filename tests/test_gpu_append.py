@@ -64,11 +64,12 @@ CASES = [
 
 @pytest.mark.parametrize("new_dtype,kv_dtype,D,Hkv", CASES)
 @pytest.mark.parametrize("special", [False, True])
-def test_append_bitexact(new_dtype, kv_dtype, D, Hkv, special):
+@pytest.mark.parametrize("P", [16, 64])
+def test_append_bitexact(new_dtype, kv_dtype, D, Hkv, special, P):
     if special and kv_dtype != FP8:
         pytest.skip("edge values matter for the fp8 conversion only")
-    rng = np.random.default_rng(100 + D + Hkv + kv_dtype)
-    B, P, maxp, npages = 23, 16, 6, 150
+    rng = np.random.default_rng(100 + D + Hkv + kv_dtype + P)
+    B, maxp, npages = 23, 6, 150
     if kv_dtype == F32:
         kv = rng.standard_normal((npages, 2, Hkv, P, D)).astype(np.float32)
     elif kv_dtype == BF16:
