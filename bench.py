@@ -554,7 +554,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b")
-    ap.add_argument("--secondary", default="skewed,mla,longfp8,llama8b-mtp2,mla-mtp2",
+    ap.add_argument("--secondary", default="tiny,skewed,mla,longfp8,llama8b-mtp2,mla-mtp2",
                     help="comma list of other workloads to report beside the headline ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
