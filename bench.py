@@ -557,6 +557,8 @@ def main():
     ap.add_argument("--heads", type=int, default=0,
                     help="query heads of the headline workload instead of its own (e.g. an MLA model's heads "
                          "on one GPU of a tensor-parallel group); 0 keeps the workload's")
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="KV heads of a GQA headline workload instead of its own; 0 keeps the workload's")
     ap.add_argument("--secondary", default="tiny,skewed,mla,longfp8,llama8b-mtp2,mla-mtp2",
                     help="comma list of other workloads to report beside the headline ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for the CPU baseline")
@@ -593,9 +595,12 @@ def main():
         runner = rows_runner(cfg, rows)
     else:
         cfg = wl.CONFIGS[args.workload]
-        if args.heads:
+        if args.heads or args.kv_heads:
             import dataclasses
-            cfg = dataclasses.replace(cfg, q_heads=args.heads)
+            if args.heads:
+                cfg = dataclasses.replace(cfg, q_heads=args.heads)
+            if args.kv_heads:
+                cfg = dataclasses.replace(cfg, kv_heads=args.kv_heads)
         runner = make_runner(cfg)
     print(f"# headline {cfg.name}: inputs generated in {runner.gen_s:.1f}s, "
           f"sum L = {runner.tokens}, {runner.bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
