@@ -235,3 +235,24 @@ def test_validate_inputs_host_checks(lib):
     assert L.decode_attn_validate_inputs(ctypes.byref(_desc(lib, num_pages=0)), None, FAKE, FAKE, None) == -2
     assert L.decode_attn_validate_inputs(None, ctypes.byref(_mla_desc(lib, batch=0)), FAKE, FAKE, None) == 0
     assert L.decode_attn_status_str(-7)
+
+
+def test_header_is_plain_c(tmp_path):
+    """decode_attn.h is a C header: it compiles as pedantic C99 with every
+    entry point taken by address."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    names = sorted(_declared())
+    src = tmp_path / "uses_header.c"
+    src.write_text('#include "decode_attn.h"\n'
+                   "int main(void) {\n"
+                   + "".join(f"    void (*p{i})(void) = (void (*)(void))&{n}; (void)p{i};\n"
+                             for i, n in enumerate(names))
+                   + "    return 0;\n}\n")
+    r = subprocess.run([gcc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror",
+                        "-I", inc, "-fsyntax-only", str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
