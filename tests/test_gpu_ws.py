@@ -144,3 +144,59 @@ def test_validate_inputs_mla():
     pt = t["page_table"].clone()
     pt[0, 0] = d.num_pages
     assert da.validate_inputs(d, pt, t["seq_lens"]) == -7
+
+
+def test_ws_calls_replay_from_a_captured_graph():
+    """The _ws calls allocate nothing and launch only kernels, so a decode step
+    can be captured into a HIP graph: every replay (with eager work and a
+    synchronisation between replays) equals the eager result bitwise."""
+    cfg = wl.GQAConfig("graph", 15, 12, 32, 8, 128, 16, wl.BF16, wl.BF16, "lognormal:900:1.0:1:6000")
+    case = wl.make_gqa_case(cfg, poison=True, seed=71)
+    t = gqa_to_dev(case)
+    workers = 512                     # explicit: no device query on the captured path
+    ref_out, ref_lse = da.decode_attn_paged(t["q"], t["kv"], t["page_table"], t["seq_lens"], case.scale,
+                                            workers=workers)
+    d = da.paged_desc(t["q"], t["kv"], t["page_table"], workers=workers)
+    ws = torch.empty(da.workspace_size(d), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(t["q"])
+    lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device="cuda")
+    da.decode_attn_paged_ws(t["q"], t["kv"], t["page_table"], t["seq_lens"], case.scale, ws, out, lse,
+                            workers=workers)                  # eager call first
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        da.decode_attn_paged_ws(t["q"], t["kv"], t["page_table"], t["seq_lens"], case.scale, ws, out, lse,
+                                workers=workers)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.zero_()                   # eager work between replays
+        lse.fill_(7.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(out), _bits(ref_out)), f"replay {rep}: out differs"
+        assert torch.equal(lse, ref_lse), f"replay {rep}: lse differs"
+
+    mcfg = wl.MLAConfig("graph", 16, 6, 128, 576, 512, 64, "lognormal:1500:1.0:1:9000")
+    mc = wl.make_mla_case(mcfg, poison=True, seed=72)
+    m = mla_to_dev(mc)
+    mref, mref_lse = da.decode_attn_mla(m["q"], m["kv"], m["page_table"], m["seq_lens"], mc.scale, workers=100)
+    md = da.MLADesc(6, 128, 576, 512, 64, m["kv"].shape[0], m["page_table"].shape[1], 100)
+    mws = torch.empty(da.workspace_size(md), dtype=torch.uint8, device="cuda")
+    mout = torch.empty((6, 128, 512), dtype=torch.bfloat16, device="cuda")
+    mlse = torch.empty((6, 128), dtype=torch.float32, device="cuda")
+    da.decode_attn_mla_ws(m["q"], m["kv"], m["page_table"], m["seq_lens"], mc.scale, mws, mout, mlse, workers=100)
+    torch.cuda.synchronize()
+    mgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(mgraph):
+        da.decode_attn_mla_ws(m["q"], m["kv"], m["page_table"], m["seq_lens"], mc.scale, mws, mout, mlse,
+                              workers=100)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        mout.zero_()
+        mlse.fill_(7.0)
+        torch.cuda.synchronize()
+        mgraph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(mout), _bits(mref)), f"MLA replay {rep}: out differs"
+        assert torch.equal(mlse, mref_lse), f"MLA replay {rep}: lse differs"
