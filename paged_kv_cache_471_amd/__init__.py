@@ -139,6 +139,75 @@ def _need_cuda(*ts):
                 raise ValueError("all tensors must be contiguous")
 
 
+_FP8 = (torch.float8_e4m3fn, torch.uint8)
+
+
+def _want(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_index_args(B: int, page_table: torch.Tensor, seq_lens: torch.Tensor, what: str = "seq_lens"):
+    """page_table int32 [B][max_pages] and seq_lens (or positions) int32 [B]."""
+    _want(page_table.dtype == torch.int32 and page_table.dim() == 2 and page_table.shape[0] == B,
+          f"page_table must be int32 [{B}][max_pages], got {page_table.dtype} {tuple(page_table.shape)}")
+    _want(page_table.shape[1] >= 1, "page_table needs at least one column")
+    _want(seq_lens.dtype == torch.int32 and tuple(seq_lens.shape) == (B,),
+          f"{what} must be int32 [{B}], got {seq_lens.dtype} {tuple(seq_lens.shape)}")
+
+
+def _check_out_lse(out: Optional[torch.Tensor], lse: Optional[torch.Tensor], out_shape, out_dtype, lse_shape):
+    if out is not None:
+        _want(out.dtype == out_dtype and tuple(out.shape) == tuple(out_shape),
+              f"out must be {out_dtype} {tuple(out_shape)}, got {out.dtype} {tuple(out.shape)}")
+    if lse is not None:
+        _want(lse.dtype == torch.float32 and tuple(lse.shape) == tuple(lse_shape),
+              f"lse must be float32 {tuple(lse_shape)}, got {lse.dtype} {tuple(lse.shape)}")
+
+
+def _check_paged_args(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                      out: Optional[torch.Tensor], lse: Optional[torch.Tensor], k_scale, v_scale):
+    """Shapes and dtypes of a GQA call, q [B][Hq][D] or [B][n][Hq][D]; raises
+    ValueError before any pointer reaches the library (which sees only
+    pointers and the descriptor)."""
+    _want(q.dim() in (3, 4), f"q must be [B][Hq][D] or [B][rows][Hq][D], got {tuple(q.shape)}")
+    _want(q.dtype in (torch.float32, torch.bfloat16), f"q must be float32 or bfloat16, got {q.dtype}")
+    B, Hq, D = q.shape[0], q.shape[-2], q.shape[-1]
+    _want(kv_pages.dim() == 5 and kv_pages.shape[1] == 2 and kv_pages.shape[4] == D,
+          f"kv_pages must be [num_pages][2][Hkv][P][{D}], got {tuple(kv_pages.shape)}")
+    Hkv = kv_pages.shape[2]
+    _want(Hkv >= 1 and Hq % Hkv == 0, f"{Hq} query heads are not a multiple of {Hkv} KV heads")
+    fp8 = kv_pages.dtype in _FP8
+    if q.dtype == torch.float32:
+        _want(kv_pages.dtype == torch.float32, f"float32 q needs a float32 cache, got {kv_pages.dtype}")
+    else:
+        _want(kv_pages.dtype == torch.bfloat16 or fp8,
+              f"bfloat16 q needs a bfloat16 or fp8-e4m3 cache, got {kv_pages.dtype}")
+    if fp8:
+        for name, sc in (("k_scale", k_scale), ("v_scale", v_scale)):
+            _want(sc is not None and sc.dtype == torch.float32 and tuple(sc.shape) == (Hkv,),
+                  f"an fp8 cache needs {name} float32 [{Hkv}], got "
+                  f"{None if sc is None else (sc.dtype, tuple(sc.shape))}")
+    else:
+        _want(k_scale is None and v_scale is None, "k_scale / v_scale apply to fp8 caches only")
+    _check_index_args(B, page_table, seq_lens)
+    _check_out_lse(out, lse, q.shape, q.dtype, q.shape[:-1])
+
+
+def _check_mla_args(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                    v_dim: int, out: Optional[torch.Tensor], lse: Optional[torch.Tensor]):
+    """Shapes and dtypes of an MLA call, q [B][H][576] or [B][n][H][576]."""
+    _want(q.dim() in (3, 4), f"q must be [B][H][Dk] or [B][rows][H][Dk], got {tuple(q.shape)}")
+    _want(q.dtype == torch.bfloat16, f"MLA q must be bfloat16, got {q.dtype}")
+    Dk = q.shape[-1]
+    _want(kv_pages.dim() == 3 and kv_pages.dtype == torch.bfloat16,
+          f"MLA kv_pages must be bfloat16 [num_pages][P][{Dk}], got {kv_pages.dtype} {tuple(kv_pages.shape)}")
+    _want(kv_pages.shape[2] == Dk, f"the cache's latent width {kv_pages.shape[2]} differs from q's {Dk}")
+    _want(1 <= v_dim <= Dk, f"v_dim {v_dim} must lie in [1, {Dk}]")
+    _check_index_args(q.shape[0], page_table, seq_lens)
+    _check_out_lse(out, lse, tuple(q.shape[:-1]) + (v_dim,), torch.bfloat16, q.shape[:-1])
+
+
 def paged_desc(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor, *, k_scale=None, v_scale=None,
                workers: int = 0) -> PagedDesc:
     B, Hq, D = q.shape
@@ -154,9 +223,12 @@ def decode_attn_paged(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch
                       k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
                       workers: int = 0, want_lse: bool = True, stream=None):
     """Paged GQA decode attention.  q [B][Hq][D] (fp32 or bf16); kv_pages
-    [num_pages][2][Hkv][16][D] (fp32, bf16, or fp8-e4m3 as float8_e4m3fn/uint8 with
-    k_scale/v_scale [Hkv] fp32); page_table int32 [B][max_pages]; seq_lens int32 [B].
+    [num_pages][2][Hkv][P][D] with P = 16, 32, ..., 256 (fp32, bf16, or fp8-e4m3 as
+    float8_e4m3fn/uint8 with k_scale/v_scale [Hkv] fp32); page_table int32
+    [B][max_pages]; seq_lens int32 [B].
     Returns (out [B][Hq][D] in q's dtype, lse [B][Hq] fp32 or None)."""
+    _want(q.dim() == 3, f"q must be [B][Hq][D], got {tuple(q.shape)}")
+    _check_paged_args(q, kv_pages, page_table, seq_lens, out, lse, k_scale, v_scale)
     _need_cuda(q, kv_pages, page_table, seq_lens, k_scale, v_scale)
     if out is None:
         out = torch.empty_like(q)
@@ -179,9 +251,10 @@ def decode_attn_paged_rows(q: torch.Tensor, kv_pages: torch.Tensor, page_table: 
     [B][n][Hq][D]: row i of request b is the token at position seq_lens[b] - n + i
     and sees positions up to its own.  Returns (out [B][n][Hq][D] in q's dtype,
     lse [B][n][Hq] fp32 or None)."""
-    _need_cuda(q, kv_pages, page_table, seq_lens, k_scale, v_scale)
     if q.dim() != 4:
         raise ValueError(f"q must be [B][rows][Hq][D], got {tuple(q.shape)}")
+    _check_paged_args(q, kv_pages, page_table, seq_lens, out, lse, k_scale, v_scale)
+    _need_cuda(q, kv_pages, page_table, seq_lens, k_scale, v_scale)
     B, n, Hq, D = q.shape
     if out is None:
         out = torch.empty_like(q)
@@ -201,6 +274,8 @@ def decode_attn_mla(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.T
                     want_lse: bool = True, stream=None):
     """Absorbed MLA decode.  q bf16 [B][H][576]; kv_pages bf16 [num_pages][P][576].
     Returns (out bf16 [B][H][v_dim], lse fp32 [B][H] or None)."""
+    _want(q.dim() == 3, f"q must be [B][H][Dk], got {tuple(q.shape)}")
+    _check_mla_args(q, kv_pages, page_table, seq_lens, v_dim, out, lse)
     _need_cuda(q, kv_pages, page_table, seq_lens)
     B, H, Dk = q.shape
     if out is None:
@@ -223,9 +298,10 @@ def decode_attn_mla_rows(q: torch.Tensor, kv_pages: torch.Tensor, page_table: to
     """Absorbed MLA decode with several query rows per request.  q bf16
     [B][n][H][576]: row i of request b sees latent positions up to
     seq_lens[b] - n + i.  Returns (out bf16 [B][n][H][v_dim], lse fp32 [B][n][H] or None)."""
-    _need_cuda(q, kv_pages, page_table, seq_lens)
     if q.dim() != 4:
         raise ValueError(f"q must be [B][rows][H][576], got {tuple(q.shape)}")
+    _check_mla_args(q, kv_pages, page_table, seq_lens, v_dim, out, lse)
+    _need_cuda(q, kv_pages, page_table, seq_lens)
     B, n, H, Dk = q.shape
     if out is None:
         out = torch.empty((B, n, H, v_dim), dtype=q.dtype, device=q.device)
@@ -242,6 +318,8 @@ def decode_attn_mla_rows(q: torch.Tensor, kv_pages: torch.Tensor, page_table: to
 
 def decode_attn_plan(seq_lens: torch.Tensor, page_size: int, units: int, workers: int, stream=None):
     """Run the split-KV planner alone; returns its outputs as int32 tensors."""
+    _want(seq_lens.dtype == torch.int32 and seq_lens.dim() == 1,
+          f"seq_lens must be int32 [B], got {seq_lens.dtype} {tuple(seq_lens.shape)}")
     _need_cuda(seq_lens)
     B = seq_lens.shape[0]
     dev = seq_lens.device
@@ -258,6 +336,8 @@ def paged_kv_gather(kv_pages: torch.Tensor, page_table: torch.Tensor, seq_lens: 
                     stream=None) -> torch.Tensor:
     """Dense copy of every live token through the kernels' address function.
     GQA: [B][max_pages*P][2][Hkv][D]; MLA: [B][max_pages*P][Dk]; rows past L are zero."""
+    _want(kv_pages.dim() == (3 if mla else 5), f"kv_pages has the wrong rank: {tuple(kv_pages.shape)}")
+    _check_index_args(page_table.shape[0] if page_table.dim() == 2 else -1, page_table, seq_lens)
     _need_cuda(kv_pages, page_table, seq_lens)
     B, maxp = page_table.shape
     if mla:
@@ -278,14 +358,25 @@ def decode_kv_append(k_new: torch.Tensor, v_new: torch.Tensor, kv_pages: torch.T
                      positions: torch.Tensor, *, k_scale: Optional[torch.Tensor] = None,
                      v_scale: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Write each request's new K/V ([B][Hkv][D], fp32 or bf16) at token positions[b]
-    of its paged history in kv_pages [num_pages][2][Hkv][16][D] (fp32, bf16, or fp8
+    of its paged history in kv_pages [num_pages][2][Hkv][P][D] (fp32, bf16, or fp8
     with k_scale/v_scale [Hkv]); a negative position skips the request.  In place;
     returns kv_pages."""
-    _need_cuda(k_new, v_new, kv_pages, page_table, positions, k_scale, v_scale)
+    _want(k_new.dim() == 3 and kv_pages.dim() == 5, "k_new must be [B][Hkv][D], kv_pages [num_pages][2][Hkv][P][D]")
     B, Hkv, D = k_new.shape
     num_pages, two, Hkv2, P, D2 = kv_pages.shape
     if two != 2 or Hkv2 != Hkv or D2 != D or tuple(v_new.shape) != (B, Hkv, D):
         raise ValueError("k_new, v_new must be [B][Hkv][D] matching kv_pages [num_pages][2][Hkv][P][D]")
+    _want(k_new.dtype == v_new.dtype and k_new.dtype in (torch.float32, torch.bfloat16),
+          f"k_new and v_new must share one dtype, float32 or bfloat16: {k_new.dtype}, {v_new.dtype}")
+    fp8 = kv_pages.dtype in _FP8
+    if fp8:
+        for name, sc in (("k_scale", k_scale), ("v_scale", v_scale)):
+            _want(sc is not None and sc.dtype == torch.float32 and tuple(sc.shape) == (Hkv,),
+                  f"an fp8 cache needs {name} float32 [{Hkv}]")
+    else:
+        _want(k_scale is None and v_scale is None, "k_scale / v_scale apply to fp8 caches only")
+    _check_index_args(B, page_table, positions, "positions")
+    _need_cuda(k_new, v_new, kv_pages, page_table, positions, k_scale, v_scale)
     d = PagedDesc(B, Hkv, Hkv, D, P, num_pages, page_table.shape[1], dtype_tag(k_new), dtype_tag(kv_pages), 0,
                   _ptr(k_scale), _ptr(v_scale))
     st = _lib.decode_kv_append(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(kv_pages), _ptr(page_table),
@@ -298,11 +389,15 @@ def decode_kv_append_mla(latent_new: torch.Tensor, kv_pages: torch.Tensor, page_
                          positions: torch.Tensor, stream=None) -> torch.Tensor:
     """Write each request's new bf16 latent ([B][576]) at token positions[b] of its
     paged history in kv_pages [num_pages][P][576]; in place; returns kv_pages."""
-    _need_cuda(latent_new, kv_pages, page_table, positions)
+    _want(latent_new.dim() == 2 and kv_pages.dim() == 3, "latent_new must be [B][576], kv_pages [num_pages][P][576]")
     B, Dk = latent_new.shape
     num_pages, P, Dk2 = kv_pages.shape
     if Dk2 != Dk:
         raise ValueError("latent_new [B][576] must match kv_pages [num_pages][P][576]")
+    _want(latent_new.dtype == torch.bfloat16 and kv_pages.dtype == torch.bfloat16,
+          f"latent_new and kv_pages must be bfloat16, got {latent_new.dtype}, {kv_pages.dtype}")
+    _check_index_args(B, page_table, positions, "positions")
+    _need_cuda(latent_new, kv_pages, page_table, positions)
     d = MLADesc(B, 128, Dk, 512, P, num_pages, page_table.shape[1], 0)
     st = _lib.decode_kv_append_mla(ctypes.byref(d), _ptr(latent_new), _ptr(kv_pages), _ptr(page_table),
                                    _ptr(positions), _stream(stream))
@@ -346,6 +441,9 @@ def decode_attn_paged_ws(q: torch.Tensor, kv_pages: torch.Tensor, page_table: to
     """decode_attn_paged / decode_attn_paged_rows with a caller-owned workspace
     (a byte tensor of at least workspace_size(...) bytes); q [B][Hq][D] or
     [B][n][Hq][D], out shaped like q.  Allocates nothing."""
+    _want(out is not None, "the _ws entry points write into a caller-owned out")
+    _check_paged_args(q, kv_pages, page_table, seq_lens, out, lse, k_scale, v_scale)
+    _want(workspace.dim() == 1, "workspace must be a flat byte tensor")
     _need_cuda(q, kv_pages, page_table, seq_lens, k_scale, v_scale, workspace, out, lse)
     q4 = _rows_view(q)
     d = paged_desc(q4[:, 0], kv_pages, page_table, k_scale=k_scale, v_scale=v_scale, workers=workers)
@@ -362,6 +460,9 @@ def decode_attn_mla_ws(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torc
                        *, v_dim: int = 512, workers: int = 0, stream=None):
     """decode_attn_mla / decode_attn_mla_rows with a caller-owned workspace;
     q [B][H][576] or [B][n][H][576].  Allocates nothing."""
+    _want(out is not None, "the _ws entry points write into a caller-owned out")
+    _check_mla_args(q, kv_pages, page_table, seq_lens, v_dim, out, lse)
+    _want(workspace.dim() == 1, "workspace must be a flat byte tensor")
     _need_cuda(q, kv_pages, page_table, seq_lens, workspace, out, lse)
     q4 = _rows_view(q)
     B, n, H, Dk = q4.shape
@@ -377,6 +478,7 @@ def decode_attn_mla_ws(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torc
 def validate_inputs(desc, page_table: torch.Tensor, seq_lens: torch.Tensor, stream=None) -> int:
     """Debug check of lengths and used page ids (synchronises); returns the
     status (0, or -7 = DA_ERR_DATA when a precondition fails)."""
+    _check_index_args(desc.batch, page_table, seq_lens)
     _need_cuda(page_table, seq_lens)
     if isinstance(desc, MLADesc):
         return _lib.decode_attn_validate_inputs(None, ctypes.byref(desc), _ptr(page_table), _ptr(seq_lens),

@@ -256,3 +256,112 @@ def test_header_is_plain_c(tmp_path):
     r = subprocess.run([gcc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror",
                         "-I", inc, "-fsyntax-only", str(src)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_mla_rows_product_that_would_wrap_is_refused(lib):
+    """batch * q_rows is formed in 64 bits: 4 * (2^30 + 1) would wrap a 32-bit
+    product to 4, a valid-looking batch; the call must be refused instead."""
+    L = lib.lib()
+    m = _mla_desc(lib, workers=32)
+    wrap = (1 << 30) + 1
+    out = ctypes.c_size_t(0)
+    assert L.decode_attn_workspace_size(None, ctypes.byref(m), wrap, ctypes.byref(out)) == -4
+    assert L.decode_attn_mla_rows(ctypes.byref(m), wrap, FAKE, FAKE, FAKE, FAKE, 0.05, FAKE, FAKE, None) == -4
+    assert L.decode_attn_mla_ws(ctypes.byref(m), wrap, FAKE, FAKE, FAKE, FAKE, 0.05, FAKE, FAKE, 0x200000,
+                                1 << 40, None) == -4
+
+
+# ---- the binding refuses tensors of the wrong shape or dtype before any
+#      pointer reaches the library (CPU tensors: shapes are checked first)
+
+def _paged_tensors(B=3, Hq=8, Hkv=2, D=64, P=16, pages=6, maxp=4, qdt=None, kvdt=None):
+    import torch
+    qdt = qdt or torch.float32
+    kvdt = kvdt or qdt
+    return dict(q=torch.zeros(B, Hq, D, dtype=qdt), kv=torch.zeros(pages, 2, Hkv, P, D, dtype=kvdt),
+                pt=torch.zeros(B, maxp, dtype=torch.int32), sl=torch.ones(B, dtype=torch.int32))
+
+
+def _mla_tensors(B=3, H=16, Dk=576, P=64, pages=6, maxp=4):
+    import torch
+    return dict(q=torch.zeros(B, H, Dk, dtype=torch.bfloat16), kv=torch.zeros(pages, P, Dk, dtype=torch.bfloat16),
+                pt=torch.zeros(B, maxp, dtype=torch.int32), sl=torch.ones(B, dtype=torch.int32))
+
+
+def test_binding_refuses_bad_gqa_arguments(lib):
+    import torch
+    t = _paged_tensors()
+    call = lambda **kw: lib.decode_attn_paged(kw.get("q", t["q"]), kw.get("kv", t["kv"]), kw.get("pt", t["pt"]),
+                                              kw.get("sl", t["sl"]), 0.125, kw.get("out"), kw.get("lse"),
+                                              k_scale=kw.get("ks"), v_scale=kw.get("vs"))
+    bad = [
+        dict(pt=t["pt"].to(torch.int64)),                              # int64 page table
+        dict(pt=torch.zeros(2, 4, dtype=torch.int32)),                 # wrong leading size
+        dict(sl=t["sl"].to(torch.int64)),
+        dict(sl=torch.ones(4, dtype=torch.int32)),
+        dict(out=torch.zeros(3, 8, 64, dtype=torch.bfloat16)),         # out dtype differs from q
+        dict(out=torch.zeros(3, 8, 32)),                               # out shape
+        dict(lse=torch.zeros(3, 8, dtype=torch.float64)),
+        dict(lse=torch.zeros(3, 4)),
+        dict(kv=torch.zeros(6, 2, 2, 16, 64, dtype=torch.bfloat16)),   # fp32 q with a bf16 cache
+        dict(kv=torch.zeros(6, 2, 3, 16, 64)),                         # 8 heads over 3 KV heads
+        dict(kv=torch.zeros(6, 2, 2, 16, 128)),                        # head_dim differs
+        dict(q=torch.zeros(3, 8, 64, dtype=torch.float16)),
+        dict(ks=torch.ones(2), vs=torch.ones(2)),                      # scales on a non-fp8 cache
+    ]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            call(**kw)
+    f8 = _paged_tensors(qdt=torch.bfloat16, kvdt=torch.uint8)
+    for ks, vs in ((None, None), (torch.ones(2), None), (torch.ones(3), torch.ones(3)),
+                   (torch.ones(2, dtype=torch.float64), torch.ones(2))):
+        with pytest.raises(ValueError):
+            lib.decode_attn_paged(f8["q"], f8["kv"], f8["pt"], f8["sl"], 0.1, k_scale=ks, v_scale=vs)
+    # well-formed arguments get past the shape checks and stop at the device check
+    with pytest.raises(ValueError, match="GPU"):
+        call()
+
+
+def test_binding_refuses_bad_mla_arguments(lib):
+    import torch
+    t = _mla_tensors()
+    call = lambda **kw: lib.decode_attn_mla(kw.get("q", t["q"]), kw.get("kv", t["kv"]), kw.get("pt", t["pt"]),
+                                            kw.get("sl", t["sl"]), 0.05, out=kw.get("out"), lse=kw.get("lse"))
+    bad = [
+        dict(kv=torch.zeros(6, 64, 512, dtype=torch.bfloat16)),        # a 512-wide cache under 576-wide q
+        dict(kv=torch.zeros(6, 64, 576, dtype=torch.float32)),
+        dict(q=torch.zeros(3, 16, 576, dtype=torch.float32)),          # fp32 q
+        dict(pt=t["pt"].to(torch.int64)),
+        dict(sl=torch.ones(2, dtype=torch.int32)),
+        dict(out=torch.zeros(3, 16, 512, dtype=torch.float32)),
+        dict(out=torch.zeros(3, 16, 576, dtype=torch.bfloat16)),
+        dict(lse=torch.zeros(3, 8)),
+    ]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            call(**kw)
+    q4 = torch.zeros(3, 2, 16, 576, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        lib.decode_attn_mla_rows(q4, torch.zeros(6, 64, 512, dtype=torch.bfloat16), t["pt"], t["sl"], 0.05)
+    with pytest.raises(ValueError):
+        lib.decode_attn_mla_rows(q4, t["kv"], t["pt"], t["sl"], 0.05, lse=torch.zeros(3, 16))
+    with pytest.raises(ValueError, match="GPU"):
+        call()
+
+
+def test_binding_refuses_bad_append_arguments(lib):
+    import torch
+    kv = torch.zeros(6, 2, 2, 16, 64, dtype=torch.bfloat16)
+    k = torch.zeros(3, 2, 64, dtype=torch.bfloat16)
+    pt, pos = torch.zeros(3, 4, dtype=torch.int32), torch.zeros(3, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        lib.decode_kv_append(k, k.float(), kv, pt, pos)                # k and v dtypes differ
+    with pytest.raises(ValueError):
+        lib.decode_kv_append(k, k, kv, pt, pos.to(torch.int64))
+    with pytest.raises(ValueError):
+        lib.decode_kv_append(k, k, kv.view(torch.int16).to(torch.uint8), pt, pos)   # fp8 cache without scales
+    lat = torch.zeros(3, 576, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        lib.decode_kv_append_mla(lat.float(), torch.zeros(6, 64, 576, dtype=torch.bfloat16), pt, pos)
+    with pytest.raises(ValueError):
+        lib.decode_kv_append_mla(lat, torch.zeros(6, 64, 576, dtype=torch.bfloat16), pt[:2], pos)
