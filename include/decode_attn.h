@@ -161,7 +161,7 @@ int decode_attn_paged(const da_paged_desc* desc, const void* q, const void* kv_p
  * decode_attn_paged_rows - decode_attn_paged with q_rows query rows per
  * request: a request's query rows in a step are one in plain decode and more
  * with multi-token prediction (MTP depth 1 gives 2) or a short prefill chunk
- * ("OpWeave", §4.2 Transition-aware scheduling, the rows q_i of each request;
+ * ("SPLASH", §4.2 Transition-aware scheduling, the rows q_i of each request;
  * "Analytical Provisioning", App. B.1).  The rows are the last q_rows tokens
  * of each history, already appended: row i sees positions
  * t <= seq_lens[b] - q_rows + i (causal among the new rows, older history
@@ -192,7 +192,7 @@ int decode_attn_mla(const da_mla_desc* desc, const void* q, const void* kv_pages
  * decode_attn_mla_rows - decode_attn_mla with q_rows query rows per request
  * (the DeepSeek-V3 configuration decodes with multi-token prediction of depth
  * 1, two rows per request: "Analytical Provisioning", App. B.1; a request's
- * query rows q_i: "OpWeave", §4.2).  Row i of request b sees latent positions
+ * query rows q_i: "SPLASH", §4.2).  Row i of request b sees latent positions
  * t <= seq_lens[b] - q_rows + i; a row that sees none gets out = 0, lse = -inf.
  *   q_rows      >= 1, with batch * q_rows <= 8192.
  *   q           device, bf16 [B][q_rows][heads][576].

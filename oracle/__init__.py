@@ -23,7 +23,7 @@ What it follows (page titles of the source material):
 * FP8 E4M3 KV carries scales (SPLASH, App. C.1 and App. B.1).
 
 * A request's query rows in a step: one in decode, the chunk length in
-  prefill; multi-token prediction of depth 1 gives two (OpWeave, §4.2;
+  prefill; multi-token prediction of depth 1 gives two (SPLASH, §4.2;
   Analytical Provisioning, App. B.1).
 
 Readings taken where the pages are silent are listed in the module docstrings

@@ -1,7 +1,7 @@
 """Multi-row decode queries, float64 (oracle; test infrastructure only).
 
 A request's query rows in one step are its chunk length in prefill and one in
-plain decode (OpWeave, §4.2 "Transition-aware scheduling": the per-request
+plain decode (SPLASH, §4.2 "Transition-aware scheduling": the per-request
 q_i beside the live context s_i).  With multi-token prediction of depth 1 a
 decode step processes 1 + 1 = 2 tokens per request (Analytical Provisioning,
 App. B.1 "Model Configuration" and the batch-size mapping that counts

@@ -32,7 +32,7 @@
 //    that the merge kernel (merge.hip) combines.
 //  * Each wave plans its own share (da_plan.h): no planner launch precedes it.
 //  * Several query rows per request (multi-token prediction, short prefill
-//    chunks: "OpWeave", §4.2, a request's query rows in a step; "Analytical
+//    chunks: "SPLASH", §4.2, a request's query rows in a step; "Analytical
 //    Provisioning", App. B.1, MTP depth 1) are the last q_rows tokens of the
 //    history; row i sees positions t <= len - q_rows + i.  The (row, head)
 //    pairs that share a KV head form the kernel's head group, so every K/V

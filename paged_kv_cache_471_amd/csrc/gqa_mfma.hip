@@ -2,7 +2,7 @@
 // (gfx950, wave64).
 //
 // Same operation, planner, partial slots and merge as gqa.hip ("OpWeave",
-// App. A.2; "SPLASH", §1 and §3; several query rows per request: "OpWeave",
+// App. A.2; "SPLASH", §1 and §3; several query rows per request: "SPLASH",
 // §4.2 and "Analytical Provisioning", App. B.1).  When many query heads share
 // a KV head (8 with an fp8 cache, or rows x heads with multi-token
 // prediction), the vector kernel spends ~680 VALU instructions per 16-token

@@ -1,7 +1,7 @@
 // Several query rows per request on the absorbed MLA path.
 //
 // A request's query rows in a step are one in plain decode, two with
-// multi-token prediction of depth 1 ("OpWeave", §4.2, the rows q_i of each
+// multi-token prediction of depth 1 ("SPLASH", §4.2, the rows q_i of each
 // request; "Analytical Provisioning", App. B.1, the DeepSeek-V3 configuration
 // with MTP depth 1).  The rows are the last ones of the history and row i sees
 // positions up to its own, so each row is a decode query over a history cut

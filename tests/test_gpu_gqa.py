@@ -85,9 +85,10 @@ def test_partitions(workers):
     assert_close_gqa(case, out, lse, ro, rl, label=f"G={workers}")
 
 
-def test_repeated_calls_reuse_counters():
-    """Split streams leave their arrival counters at zero: many calls in a row,
-    with different shapes, all match the oracle."""
+def test_repeated_calls_reuse_workspace():
+    """The library's workspace carries nothing from one call to the next that
+    a later call reads before writing: many calls in a row over the same
+    buffer, with different lengths and worker counts, all match the oracle."""
     cfg = _cfg(wl.BF16, wl.BF16, 32, 8, 128, "lognormal:900:1.0:1:9000", B=12)
     cases = [wl.make_gqa_case(cfg, poison=True, seed=200 + i) for i in range(3)]
     refs = [gqa_oracle(c) for c in cases]
