@@ -71,6 +71,27 @@ def test_trace_moments_meet_corollary_4_5_on_long_geometric_traces():
     assert abs(var - v) / v < 0.05
 
 
+@pytest.mark.parametrize("mu_d", [1.0, 2.0, 37.5, 500.0])
+def test_corollary_4_5_against_exact_sums_over_the_lifetime_law(mu_d):
+    """Stationary load Y = P + A, P independent of the request's age A.  A
+    uniformly random decode step lands in a request with probability
+    proportional to its lifetime D (length biasing), at an age uniform on
+    0..D-1: E[A] = E[D(D-1)/2] / E[D], E[A^2] = E[(D-1)D(2D-1)/6] / E[D].  For
+    geometric D on {1, 2, ...} these sums are taken term by term over the pmf
+    (truncated where the tail is below 1e-30), not sampled."""
+    p = 1.0 / mu_d
+    d = np.arange(1, 200001, dtype=np.float64)
+    pmf = p * (1.0 - p) ** (d - 1)
+    assert pmf[-1] < 1e-30 and abs(pmf.sum() - 1) < 1e-12
+    ed = (pmf * d).sum()
+    ea = (pmf * d * (d - 1) / 2).sum() / ed
+    ea2 = (pmf * (d - 1) * d * (2 * d - 1) / 6).sum() / ed
+    mu_p, var_p = 100.0, 100.0 * 101.0
+    theta, nu2 = pv.geometric_slot_moments(mu_p, var_p, mu_d)
+    assert abs(theta - (mu_p + ea)) < 1e-9 * max(1.0, theta)
+    assert abs(nu2 - (var_p + ea2 - ea * ea)) < 1e-9 * max(1.0, nu2)
+
+
 def test_trace_moments_by_hand():
     # requests (P, D): (3, 2) -> loads 3, 4; (0, 3) -> 0, 1, 2; (5, 1) -> 5
     theta, q, var = pv.stationary_moments([3, 0, 5], [2, 3, 1])
@@ -94,14 +115,72 @@ def test_fit_recovers_an_exact_line():
     assert abs(a - 3.5e-9) < 1e-18 and abs(b - 4e-6) < 1e-15
 
 
-def test_planted_mistakes_are_caught():
-    g = json.load(open(GOLDEN))
-    # arrival-average load mu_P + mu_D without length biasing: nu^2 would be sigma_P^2 + sigma_D^2 / ...
-    # a dropped sqrt(B) in the overhead misses the printed column by far
-    theta, nu = 600.0, math.sqrt(100 * 101 + 500 * 501)
-    wrong = 100 * math.sqrt(256) * nu * pv.kappa(8) / (256 * theta) / math.sqrt(256)
-    assert abs(wrong - g["rows"][2]["clt"]) > 1.0
-    # the timeline with ages 1..D instead of 0..D-1 shifts theta by exactly 1
-    theta0, _, _ = pv.stationary_moments([3, 0, 5], [2, 3, 1])
-    shifted = np.mean([4, 5, 1, 2, 3, 6])
-    assert shifted - theta0 == 1.0
+def _pins():
+    """The pins above as callables, so that a planted mistake can be run
+    through them; each raises AssertionError when its check fails."""
+    return {
+        "kappa closed forms": test_kappa_closed_forms,
+        "printed CLT column": test_barrier_overhead_reproduces_the_printed_clt_column,
+        "Corollary 4.5": test_trace_moments_meet_corollary_4_5_on_long_geometric_traces,
+        "exact lifetime sums": lambda: [test_corollary_4_5_against_exact_sums_over_the_lifetime_law(m)
+                                        for m in (1.0, 2.0, 37.5, 500.0)],
+        "hand sums": test_trace_moments_by_hand,
+        "timeline walk": test_load_at_step_walks_the_timeline,
+        "exact line": test_fit_recovers_an_exact_line,
+    }
+
+
+def _failing_pins():
+    failed = []
+    for name, pin in _pins().items():
+        try:
+            pin()
+        except AssertionError:
+            failed.append(name)
+    return failed
+
+
+def test_pins_pass_on_the_oracle_as_written():
+    assert _failing_pins() == []
+
+
+def _wrong_kappa(r):
+    # integrand with Phi^r instead of Phi^(r-1)
+    import scipy.integrate
+    import scipy.stats
+    f = lambda z: z * r * scipy.stats.norm.pdf(z) * scipy.stats.norm.cdf(z) ** r
+    return scipy.integrate.quad(f, -np.inf, np.inf, epsabs=1e-13, epsrel=1e-13, limit=200)[0]
+
+
+def _timeline_ages_from_one(P, D):
+    out = []
+    for p, d in zip(np.asarray(P).tolist(), np.asarray(D).tolist()):
+        out.extend(range(p + 1, p + d + 1))
+    return np.array(out, dtype=np.int64)
+
+
+def _fit_without_intercept(T, t):
+    T = np.asarray(T, dtype=np.float64)
+    t = np.asarray(t, dtype=np.float64)
+    return float((T * t).sum() / (T * T).sum()), 0.0
+
+
+@pytest.mark.parametrize("name,fn,caught_by", [
+    # the sqrt(B) of the worker-load spread dropped from the overhead
+    ("barrier_overhead", lambda B, th, nu, r: nu * pv.kappa(r) / (B * th), "printed CLT column"),
+    # the spread counted per slot instead of per worker (B instead of sqrt(B))
+    ("barrier_overhead", lambda B, th, nu, r: B * nu * pv.kappa(r) / (B * th), "printed CLT column"),
+    ("kappa", _wrong_kappa, "kappa closed forms"),
+    # Corollary 4.5 with mu_out = E[D] instead of E[D] - 1
+    ("geometric_slot_moments", lambda mp, vp, md: (mp + md, vp + md * (md + 1.0)), "exact lifetime sums"),
+    # the age variance dropped (nu^2 = sigma_P^2 only)
+    ("geometric_slot_moments", lambda mp, vp, md: (mp + md - 1.0, vp), "Corollary 4.5"),
+    ("slot_timeline", _timeline_ages_from_one, "hand sums"),
+    ("fit_linear", _fit_without_intercept, "exact line"),
+])
+def test_planted_mistakes_in_the_oracle_are_caught(monkeypatch, name, fn, caught_by):
+    """Plant a plausible mistake into oracle/provision.py itself and run the
+    pins: the named pin must fail."""
+    monkeypatch.setattr(pv, name, fn)
+    failed = _failing_pins()
+    assert caught_by in failed, f"planting a wrong {name} left every pin green: {failed}"
