@@ -99,12 +99,56 @@ size_t split_layout(int streams, int G, int heads, int dim, char* base, SplitBuf
     return off;
 }
 
+// The 128-head MLA kernel keeps one slot per piece (index request + worker,
+// below batch + workers) of raw [128][512] fp32 accumulators and [128] (max,
+// sum) pairs, plus a [128][512] scratch area per worker.
+size_t mla_wave_layout(int batch, int G, char* base, SplitBuffers* sb, float** tmp, size_t extra_ints = 0) {
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> char* {
+        char* p = base ? base + off : nullptr;
+        off = round_up(off + bytes, 256);
+        return p;
+    };
+    const size_t slots = static_cast<size_t>(batch) + G;
+    const size_t tile = static_cast<size_t>(da::kMlaWaveHeads) * da::kMlaV;
+    SplitBuffers t;
+    t.plan_info = reinterpret_cast<int2*>(take(sizeof(int2)));
+    t.stream_info = reinterpret_cast<int2*>(take(sizeof(int2) * static_cast<size_t>(batch)));
+    t.o_part = reinterpret_cast<float*>(take(sizeof(float) * slots * tile));
+    t.lse_part = reinterpret_cast<float*>(take(sizeof(float) * 2 * slots * da::kMlaWaveHeads));
+    float* tp = reinterpret_cast<float*>(take(sizeof(float) * static_cast<size_t>(G) * tile));
+    t.extra = extra_ints ? reinterpret_cast<int32_t*>(take(sizeof(int32_t) * extra_ints)) : nullptr;
+    if (sb) *sb = t;
+    if (tmp) *tmp = tp;
+    return off;
+}
+
 // A workspace the caller owns (the _ws entry points): used as given, never
 // grown; the library allocates nothing on that path.
 struct CallerWorkspace {
     void* ptr;
     size_t bytes;
 };
+
+// Carves the buffers of one call out of the caller's workspace or the
+// library's: `layout(base)` returns the bytes needed (base null) or fills the
+// pointers.
+template <class Layout>
+int get_buffers(hipStream_t s, const CallerWorkspace* cws, Layout&& layout) {
+    const size_t need = layout(nullptr);
+    void* base = nullptr;
+    if (cws != nullptr) {
+        if (cws->ptr == nullptr) return DA_ERR_NULL;
+        if (!aligned(cws->ptr, 256)) return DA_ERR_SHAPE;
+        if (cws->bytes < need) return DA_ERR_WORKSPACE;
+        base = cws->ptr;
+    } else {
+        int st = get_workspace(s, need, &base);
+        if (st != DA_OK) return st;
+    }
+    layout(static_cast<char*>(base));
+    return DA_OK;
+}
 
 int get_split_buffers(hipStream_t s, int streams, int G, int heads, int dim, SplitBuffers* sb,
                       size_t extra_ints = 0, const CallerWorkspace* cws = nullptr) {
@@ -267,7 +311,8 @@ int resolve_mla_workers(const da_mla_desc* d, int* G) {
     int cus = 0;
     int st = device_cus(&cus);
     if (st != DA_OK) return st;
-    int g = cus * da::mla_blocks_per_cu() / da::mla_blocks_per_worker(d->num_heads);
+    int g = d->num_heads == da::kMlaWaveHeads ? cus * da::mla_wave_blocks_per_cu()
+                                              : cus * da::mla_blocks_per_cu() / da::mla_blocks_per_worker(d->num_heads);
     if (g <= 0) return DA_ERR_UNSUPPORTED;
     if (g > da::kMlaMaxWorkers) g = da::kMlaMaxWorkers;
     *G = g;
@@ -295,9 +340,12 @@ int mla_workspace_bytes(const da_mla_desc* dd, int q_rows, size_t* bytes) {
     int st = check_mla(dd);
     if (st != DA_OK) return st;
     if (q_rows < 1) return DA_ERR_SHAPE;
+    // rows run as batch * q_rows requests: form the product in 64 bits so that
+    // no q_rows can wrap it into a small, valid-looking batch
+    const int64_t expanded = static_cast<int64_t>(dd->batch) * q_rows;
+    if (expanded > da::kMaxBatch) return DA_ERR_UNSUPPORTED;
     da_mla_desc rd = *dd;
-    rd.batch = dd->batch * q_rows;
-    if (rd.batch > da::kMaxBatch) return DA_ERR_UNSUPPORTED;
+    rd.batch = static_cast<int32_t>(expanded);
     if (static_cast<int64_t>(rd.batch) * rd.max_pages_per_seq >= (int64_t(1) << 31)) return DA_ERR_UNSUPPORTED;
     *bytes = 0;
     if (rd.batch == 0) return DA_OK;
@@ -305,7 +353,8 @@ int mla_workspace_bytes(const da_mla_desc* dd, int q_rows, size_t* bytes) {
     st = resolve_mla_workers(&rd, &G);
     if (st != DA_OK) return st;
     const size_t extra = q_rows > 1 ? static_cast<size_t>(rd.batch) * (1 + rd.max_pages_per_seq) : 0;
-    *bytes = split_layout(rd.batch, G, rd.num_heads, rd.v_dim, nullptr, nullptr, extra);
+    *bytes = rd.num_heads == da::kMlaWaveHeads ? mla_wave_layout(rd.batch, G, nullptr, nullptr, nullptr, extra)
+                                               : split_layout(rd.batch, G, rd.num_heads, rd.v_dim, nullptr, nullptr, extra);
     return DA_OK;
 }
 
@@ -401,9 +450,12 @@ int mla_step(const da_mla_desc* dd, int q_rows, const void* q, const void* kv_pa
     int st = check_mla(dd);
     if (st != DA_OK) return st;
     if (q_rows < 1) return DA_ERR_SHAPE;
+    // rows run as batch * q_rows requests: form the product in 64 bits so that
+    // no q_rows can wrap it into a small, valid-looking batch
+    const int64_t expanded = static_cast<int64_t>(dd->batch) * q_rows;
+    if (expanded > da::kMaxBatch) return DA_ERR_UNSUPPORTED;
     da_mla_desc rd = *dd;
-    rd.batch = dd->batch * q_rows;
-    if (rd.batch > da::kMaxBatch) return DA_ERR_UNSUPPORTED;
+    rd.batch = static_cast<int32_t>(expanded);
     if (static_cast<int64_t>(rd.batch) * rd.max_pages_per_seq >= (int64_t(1) << 31)) return DA_ERR_UNSUPPORTED;
     const da_mla_desc* d = &rd;
     if (q == nullptr || kv_pages == nullptr || page_table == nullptr || seq_lens == nullptr || out == nullptr)
@@ -419,8 +471,13 @@ int mla_step(const da_mla_desc* dd, int q_rows, const void* q, const void* kv_pa
     st = resolve_mla_workers(d, &G);
     if (st != DA_OK) return st;
     SplitBuffers sb;
+    float* tmp = nullptr;
+    const bool wave = d->num_heads == da::kMlaWaveHeads;
     const size_t extra = q_rows > 1 ? static_cast<size_t>(d->batch) * (1 + d->max_pages_per_seq) : 0;
-    st = get_split_buffers(s, d->batch, G, d->num_heads, d->v_dim, &sb, extra, cws);
+    if (wave)
+        st = get_buffers(s, cws, [&](char* base) { return mla_wave_layout(d->batch, G, base, &sb, &tmp, extra); });
+    else
+        st = get_split_buffers(s, d->batch, G, d->num_heads, d->v_dim, &sb, extra, cws);
     if (st != DA_OK) return st;
     if (q_rows > 1) {
         da::RowsArgs ra{};
@@ -455,6 +512,14 @@ int mla_step(const da_mla_desc* dd, int q_rows, const void* q, const void* kv_pa
     ma.lse = lse;
     ma.o_part = sb.o_part;
     ma.lse_part = sb.lse_part;
+    ma.o_tmp = tmp;
+    if (wave) {
+        hipError_t e = da::launch_mla_wave(ma, s, next_kernel_events());
+        if (e != hipSuccess) return hip_fail(e);
+        e = da::launch_mla_wave_merge(ma, s);
+        if (e != hipSuccess) return hip_fail(e);
+        return DA_OK;
+    }
     hipError_t e = da::launch_mla(ma, s, next_kernel_events());
     if (e != hipSuccess) return hip_fail(e);
 

@@ -74,6 +74,11 @@ struct MlaArgs {
     float* lse;             // fp32 [batch][heads] or null
     float* o_part;          // [2 * workers][heads][512]
     float* lse_part;        // [2 * workers][heads]   (log2 domain)
+    // The 128-head kernel (mla_wave.hip) uses instead one slot per piece,
+    // index b + worker: o_part [batch + workers][128][512] raw accumulator
+    // tiles, lse_part [batch + workers][128][2] (running max in log2, sum),
+    // and o_tmp [workers][128][512] as scratch.
+    float* o_tmp;
 };
 
 // Log-sum-exp merge of the partial slots of split streams.  One workgroup per
@@ -116,6 +121,12 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, int streams, hipStream_t s);
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t s, const KernelEvents& ev);
+// The 128-head kernel (mla_wave.hip) and its merge, which normalises every
+// request from its per-piece slots (whole requests included).
+hipError_t launch_mla_wave(const MlaArgs& a, hipStream_t s, const KernelEvents& ev);
+hipError_t launch_mla_wave_merge(const MlaArgs& a, hipStream_t s);
+int mla_wave_blocks_per_cu();
+constexpr int kMlaWaveHeads = 128;
 // Workgroups of the MLA kernel that fit on one CU at once.
 int mla_blocks_per_cu();
 // Head counts with an MLA kernel (16, 32, 64, 128).

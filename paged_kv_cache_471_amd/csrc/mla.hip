@@ -46,27 +46,16 @@
 //    partials go to a slot that the merge kernel (merge.hip) combines.
 #include <hip/hip_ext.h>
 
-#include "da_common.h"
-#include "da_launch.h"
-#include "da_plan.h"
+#include "da_mla.h"
 
 namespace da {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx4_t __attribute__((ext_vector_type(4)));
-typedef float floatx16_t __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 constexpr int kWaves = 8;
 constexpr int kBlock = kWaves * 64;
-constexpr int kRowBytes = kMlaLatent * 2;             // 1152 bytes per token in HBM
-constexpr int kXB = kRowBytes / 16;                   // 72 16-byte blocks per token
-constexpr int kSlotBytes = kXB * kMlaChunk * 16;      // 36864
-constexpr int kSlotLoads = kSlotBytes / 1024;         // 36 wave-wide 16-byte loads
 constexpr int kLoaders = 4;                           // waves that issue the chunk loads
-constexpr int kLoadsPerLoader = kSlotLoads / kLoaders;   // 9
-static_assert(kSlotLoads % kLoaders == 0 && kLoaders % 2 == 0, "loader split");
+constexpr int kLoadsPerLoader = kMlaSlotLoads / kLoaders;   // 9
+static_assert(kMlaSlotLoads % kLoaders == 0 && kLoaders % 2 == 0, "loader split");
 constexpr int kSlots = 4;
 constexpr int kHG = kMlaMaxHeads;                     // heads per workgroup
 constexpr int kPRow = 80;                             // bytes per head row of P (64 + 16 pad)
@@ -91,133 +80,11 @@ constexpr int kFlagOff = kFinOff + kHW * 4;           // 1408
 static_assert(kFlagOff + 4 <= kArea && 2 * 64 * 16 == kArea, "area layout");
 
 struct __align__(16) Smem {
-    char ring[kSlots][kSlotBytes];
+    char ring[kSlots][kMlaSlotBytes];
     char area[kWaves][kArea];
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS");
 
-// Compute/load cursor over the chunks of a worker's share.  Wave-uniform.
-struct Cursor {
-    int b, p, ci;      // request, page, chunk within the page
-    int len, pages;    // request length and page count
-    int nch;           // chunks of page p holding live tokens
-    int k;             // unit (page) index within the share
-};
-
-__device__ __forceinline__ int chunks_of_page(int len, int p, int P) {
-    const int live = min(P, len - p * P);
-    return (live + kMlaChunk - 1) / kMlaChunk;
-}
-
-__device__ __forceinline__ void cursor_init(Cursor& c, const WaveShare& sh, const int32_t* seq_lens, int P) {
-    c.b = sh.b;
-    c.p = sh.p;
-    c.ci = 0;
-    c.len = sload_i32(seq_lens + c.b);
-    c.pages = (c.len + P - 1) / P;
-    c.nch = chunks_of_page(c.len, c.p, P);
-    c.k = 0;
-}
-
-// Advance one chunk.  Moving past the share's last unit leaves k == n and
-// reads nothing.
-__device__ __forceinline__ void cursor_next(Cursor& c, const int32_t* seq_lens, int P, int n) {
-    if (++c.ci < c.nch) return;
-    c.ci = 0;
-    if (++c.k >= n) return;
-    if (++c.p >= c.pages) {
-        c.p = 0;
-        do {
-            ++c.b;
-            c.len = sload_i32(seq_lens + c.b);
-            c.pages = (c.len + P - 1) / P;
-        } while (c.pages == 0);
-    }
-    c.nch = chunks_of_page(c.len, c.p, P);
-}
-
-// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane.
-// Written as inline assembly so that the compiler, which cannot tell which
-// LDS bytes such a load writes, does not drain every outstanding load before
-// each LDS access; completion is tracked with wait_vmcnt below instead.
-// m0 is listed as clobbered (the compiler warns that it is a reserved
-// register): on gfx950 LDS instructions do not read m0, and the built kernels
-// contain no m0 access other than these blocks' own writes.
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "s"(lds_addr)
-                 : "memory", "m0");
-}
-
-// Wait until at most N vector memory operations of this wave are outstanding.
-// Loads complete in issue order, so this makes every load issued before the
-// last N complete.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt immediate");
-    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
-// Workgroup barrier for LDS traffic only (does not wait for global loads).
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
-}
-
-// Start the scalar read of *next_pid, wait until at most N vector memory
-// operations of this wave are outstanding (the chunk about to be computed has
-// landed), then meet the workgroup at a barrier.  The page-id read overlaps
-// the wait for the chunk instead of stalling the wave on its own.
-template <int N>
-__device__ __forceinline__ int wait_chunk_barrier(const int32_t* next_pid) {
-    int v;
-    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt vmcnt(%2)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier"
-                 : "=s"(v)
-                 : "s"(next_pid), "n"(N)
-                 : "memory");
-    return v;
-}
-
-typedef short short4v __attribute__((ext_vector_type(4)));
-
-// Reductions over the lane pairs (l, l ^ 16) and (l, l ^ 32) with the gfx950
-// row swaps: after swapping a value with itself, the two results hold the
-// values of both lanes of each pair, in one order or the other, so max and
-// sum of the two are the pairwise max and sum (no LDS round trip).
-__device__ __forceinline__ float max_xor16(float x) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_xor32(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_xor16(float x) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float sum_xor32(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Two fp32 values -> packed bf16 pair (round to nearest even), one conversion.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2_t));
-}
-
-// Transposing 8-byte LDS read (gfx950): see the value-operand note in the kernel.
-__device__ __forceinline__ short4v ds_read_tr16(const char* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p));
-}
-
-__device__ __forceinline__ floatx16_t mfma32(bf16x8_t a, bf16x8_t b, floatx16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ floatx4_t mfma16(bf16x8_t a, bf16x8_t b, floatx4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 
 template <int H>
 __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
@@ -264,15 +131,15 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
     //      token t = t' ^ 4 ((2 q + half) & 3), and (2 q) & 3 = 2 (w & 1) for
     //      every i.
     const bool loader = w < kLoaders;
-    Cursor lc;
-    cursor_init(lc, sh, a.seq_lens, P);
+    MlaCursor lc;
+    mla_cursor_init(lc, sh, a.seq_lens, P);
     int issued = 0;                                             // chunks issued so far
     // source of this lane's part of the next chunk to load (page pid)
     auto dma_src = [&](int pid) {
         int ln = lane;
         asm volatile("" : "+v"(ln));      // recomputed per chunk rather than held in a register
-        const int dma_off = ((ln & 31) ^ (((2 * (w & 1) + (ln >> 5)) & 3) << 2)) * kRowBytes + (ln >> 5) * 16;
-        return kvb + (static_cast<int64_t>(pid) * P + lc.ci * kMlaChunk) * kRowBytes + dma_off;
+        const int dma_off = ((ln & 31) ^ (((2 * (w & 1) + (ln >> 5)) & 3) << 2)) * kMlaRowBytes + (ln >> 5) * 16;
+        return kvb + (static_cast<int64_t>(pid) * P + lc.ci * kMlaChunk) * kMlaRowBytes + dma_off;
     };
     auto dma_lds = [&]() {
         return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)sm.ring[issued % kSlots]));
@@ -280,11 +147,11 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
     // load j (0..8) of this loader wave's share of the chunk
     auto dma_load = [&](const char* src, uint32_t lds_base, int j) {
         const int q = w + kLoaders * j;
-        lds_dma16(src + 32 * q, lds_base + q * 1024);
+        mla_lds_dma16(src + 32 * q, lds_base + q * 1024);
     };
     auto chunk_issued = [&]() {
         ++issued;
-        cursor_next(lc, a.seq_lens, P, n);
+        mla_cursor_next(lc, a.seq_lens, P, n);
     };
     auto issue_chunk = [&](int pid) {
         if (loader) {
@@ -372,8 +239,8 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
                 for (int r = 0; r < 16; ++r) acc[hb][db][r] = 0.0f;
     };
 
-    Cursor cc;
-    cursor_init(cc, sh, a.seq_lens, P);
+    MlaCursor cc;
+    mla_cursor_init(cc, sh, a.seq_lens, P);
     int piece_first_unit = 0;             // k of the piece's first unit
     int piece_p0 = cc.p;                  // first page of the piece within its request
     bool first_piece = true;
@@ -398,9 +265,9 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
             const int after = issued - 1 - i;
             const int32_t* pa = next_pid_addr();                // valid even past the share's end
             int pid;
-            if (after >= 2) pid = loader ? wait_chunk_barrier<2 * kLoadsPerLoader>(pa) : wait_chunk_barrier<0>(pa);
-            else if (after == 1) pid = loader ? wait_chunk_barrier<kLoadsPerLoader>(pa) : wait_chunk_barrier<0>(pa);
-            else pid = wait_chunk_barrier<0>(pa);
+            if (after >= 2) pid = loader ? mla_wait_chunk_barrier<2 * kLoadsPerLoader>(pa) : mla_wait_chunk_barrier<0>(pa);
+            else if (after == 1) pid = loader ? mla_wait_chunk_barrier<kLoadsPerLoader>(pa) : mla_wait_chunk_barrier<0>(pa);
+            else pid = mla_wait_chunk_barrier<0>(pa);
             // The loads of chunk i+3 (into the slot chunk i-1 used) are spread
             // over the score product: a wave that issues them in one burst
             // waits while the memory pipeline takes each 1 KiB load in turn.
@@ -471,7 +338,7 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
                 }
             }
             if (more) chunk_issued();
-            lds_barrier();                                      // partial scores exchanged
+            mla_lds_barrier();                                      // partial scores exchanged
 
             // ---- softmax for this wave's 16 heads
             if (s_active) {
@@ -522,7 +389,7 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
                 const bool moved = __ballot(alpha != 1.0f) != 0ull;
                 if (lane == 0) *reinterpret_cast<int*>(xa + w * kArea + kFlagOff) = moved;
             }
-            lds_barrier();                                      // B2: P, alpha and flags visible
+            mla_lds_barrier();                                      // B2: P, alpha and flags visible
 
             // ---- value update for dims [dw, dw + 64) of every head
             const int oln = fresh_lane();
@@ -569,7 +436,7 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
             stream_end = page_end && cc.p == cc.pages - 1;
             share_end = page_end && cc.k == n - 1;
             if (stream_end || share_end) break;
-            cursor_next(cc, a.seq_lens, P, n);
+            mla_cursor_next(cc, a.seq_lens, P, n);
         }
         ++i;
 
@@ -636,7 +503,7 @@ __global__ __launch_bounds__(kBlock, 1) void mla_attn_kernel(MlaArgs a) {
             a.stream_info[b] = make_int2(static_cast<int>(start), gl - gf + 1);
         }
         __syncthreads();                                        // final sums read before areas are reused
-        cursor_next(cc, a.seq_lens, P, n);
+        mla_cursor_next(cc, a.seq_lens, P, n);
         first_piece = false;
         piece_p0 = 0;
         piece_first_unit = cc.k;

@@ -160,3 +160,27 @@ def test_full_size_sampled():
                   set(int(x) for x in np.random.default_rng(0).choice(len(L), size=4, replace=False)))
     ro, rl = oracle_of(case, requests=reqs)
     assert_close(case, out, lse, ro, rl, requests=reqs, label="mla full")
+
+
+@pytest.mark.parametrize("H", [64, 128])
+@pytest.mark.parametrize("workers", [0, 3, 11])
+def test_running_max_jumps_every_chunk(H, workers):
+    """Scores that rise by more than the kernels' raise margin at every chunk
+    boundary: the running maximum moves on every chunk, so the 128-head kernel
+    folds its accumulators into the piece's slot and restarts on every chunk
+    (and the 64-head kernel rescales on every chunk).  The growth sits in the
+    64 rope dims of the latent, which are keys only: rope part of latent row t
+    is (t / 2) u, every head's query rope part is u, so scores rise by about 15
+    (base 2) per 32 tokens while the values stay N(0, 0.5)."""
+    cfg = _cfg(H=H, lengths="uniform:150:700", B=3)
+    case = wl.make_mla_case(cfg, poison=True, extra_pages=1, seed=91 + H)
+    rng = np.random.default_rng(5)
+    u = rng.standard_normal(64) * 0.5
+    for b, L in enumerate(case.seq_lens):
+        for t in range(int(L)):
+            pg, r = case.page_table[b, t // cfg.page_size], t % cfg.page_size
+            case.kv[pg, r, 512:] = wl.to_bf16_bits(u * (t / 2.0))
+    case.q[:, :, 512:] = wl.to_bf16_bits(np.broadcast_to(u, case.q[:, :, 512:].shape))
+    out, lse = run(case, workers=workers)
+    ro, rl = oracle_of(case)
+    assert_close(case, out, lse, ro, rl, label=f"jumps H{H} G{workers}")
