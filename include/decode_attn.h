@@ -69,6 +69,7 @@ extern "C" {
 #define DA_ERR_WORKSPACE   -5   /* workspace could not be allocated */
 #define DA_ERR_HIP         -6   /* a HIP call failed; see decode_attn_last_hip_error() */
 #define DA_ERR_DATA        -7   /* decode_attn_validate_inputs: device data breaks a precondition */
+#define DA_ERR_SCRATCH     -8   /* decode_attn_paged_noalloc: the call needs more than its static scratch */
 
 /* storage dtype tags */
 #define DA_F32       0          /* IEEE binary32 */
@@ -313,6 +314,33 @@ int decode_attn_paged_ws(const da_paged_desc* desc, int32_t q_rows, const void* 
 int decode_attn_mla_ws(const da_mla_desc* desc, int32_t q_rows, const void* q, const void* kv_pages,
                        const int32_t* page_table, const int32_t* seq_lens, float scale, void* out, float* lse,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * decode_attn_paged_noalloc - for callers that cannot allocate device memory
+ * and cannot hand in a workspace either (code under stream or graph capture,
+ * tight serving loops, harnesses that forbid allocation): decode_attn_paged_rows
+ * (q_rows = 1 is decode_attn_paged) whose workspace is a fixed scratch array
+ * the library holds in device memory, DA_NOALLOC_SCRATCH_BYTES per device.
+ * Each device that runs the library keeps its own copy from the moment the
+ * library's code is loaded onto it until the process ends.
+ *   Arguments, layouts and results as decode_attn_paged_rows; the results are
+ *   bitwise those of decode_attn_paged_ws with the same descriptor (workers
+ *   included).
+ *   Makes no hipMalloc / hipFree and calls no allocating library routine.
+ *   Errors: those of decode_attn_paged_rows, plus DA_ERR_SCRATCH when
+ *   decode_attn_workspace_size for this call exceeds DA_NOALLOC_SCRATCH_BYTES
+ *   (before any launch; smaller batches or fewer workers fit), and DA_ERR_HIP
+ *   if the scratch address cannot be obtained on the current device.
+ * Every call on one device shares that device's scratch: calls that may
+ * overlap in time on one device (different streams, or host threads without
+ * ordering) race and give wrong results; order them on one stream.  Nothing
+ * in the scratch needs an initial value (each call writes what it later
+ * reads), so leftovers of an earlier call do no harm.
+ */
+#define DA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int decode_attn_paged_noalloc(const da_paged_desc* desc, int32_t q_rows, const void* q, const void* kv_pages,
+                              const int32_t* page_table, const int32_t* seq_lens, float scale, void* out,
+                              float* lse, void* stream);
 
 /*
  * decode_attn_validate_inputs - debug check of the data-dependent

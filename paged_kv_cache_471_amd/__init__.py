@@ -19,13 +19,15 @@ LIB_PATH = os.path.join(_HERE, "libdecode_attn.so")
 
 DA_F32, DA_BF16, DA_FP8_E4M3 = 0, 1, 2
 STATUS = {0: "DA_OK", -1: "DA_ERR_NULL", -2: "DA_ERR_SHAPE", -3: "DA_ERR_DTYPE", -4: "DA_ERR_UNSUPPORTED",
-          -5: "DA_ERR_WORKSPACE", -6: "DA_ERR_HIP", -7: "DA_ERR_DATA"}
+          -5: "DA_ERR_WORKSPACE", -6: "DA_ERR_HIP", -7: "DA_ERR_DATA",
+          -8: "DA_ERR_SCRATCH"}
 
 EXPORTS = ("decode_attn_paged", "decode_attn_paged_rows", "decode_attn_mla", "decode_attn_mla_rows", "decode_attn_plan", "paged_kv_gather",
            "decode_kv_append", "decode_kv_append_mla",
            "decode_attn_default_workers", "decode_attn_status_str", "decode_attn_last_hip_error",
            "decode_attn_timer_begin", "decode_attn_timer_end",
-           "decode_attn_workspace_size", "decode_attn_paged_ws", "decode_attn_mla_ws", "decode_attn_validate_inputs")
+           "decode_attn_workspace_size", "decode_attn_paged_ws", "decode_attn_mla_ws", "decode_attn_validate_inputs",
+           "decode_attn_paged_noalloc")
 
 
 class PagedDesc(ctypes.Structure):
@@ -91,6 +93,8 @@ def _load():
     lib.decode_attn_paged_ws.restype = ctypes.c_int
     lib.decode_attn_mla_ws.argtypes = [ctypes.POINTER(MLADesc), i32, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp]
     lib.decode_attn_mla_ws.restype = ctypes.c_int
+    lib.decode_attn_paged_noalloc.argtypes = [ctypes.POINTER(PagedDesc), i32, vp, vp, vp, vp, f32, vp, vp, vp]
+    lib.decode_attn_paged_noalloc.restype = ctypes.c_int
     lib.decode_attn_validate_inputs.argtypes = [ctypes.POINTER(PagedDesc), ctypes.POINTER(MLADesc), vp, vp, vp]
     lib.decode_attn_validate_inputs.restype = ctypes.c_int
     return lib
@@ -455,6 +459,29 @@ def decode_attn_paged_ws(q: torch.Tensor, kv_pages: torch.Tensor, page_table: to
     return out, lse
 
 
+# bytes of the device scratch array behind decode_attn_paged_noalloc (one per device)
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def decode_attn_paged_noalloc(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor,
+                              seq_lens: torch.Tensor, scale: float, out: torch.Tensor,
+                              lse: Optional[torch.Tensor] = None, *, k_scale: Optional[torch.Tensor] = None,
+                              v_scale: Optional[torch.Tensor] = None, workers: int = 0, stream=None):
+    """decode_attn_paged / decode_attn_paged_rows for callers that cannot
+    allocate: the workspace is the library's static per-device scratch
+    (NOALLOC_SCRATCH_BYTES); q [B][Hq][D] or [B][n][Hq][D], out shaped like q
+    and owned by the caller.  Calls that may overlap on one device race."""
+    _want(out is not None, "decode_attn_paged_noalloc writes into a caller-owned out")
+    _check_paged_args(q, kv_pages, page_table, seq_lens, out, lse, k_scale, v_scale)
+    _need_cuda(q, kv_pages, page_table, seq_lens, k_scale, v_scale, out, lse)
+    q4 = _rows_view(q)
+    d = paged_desc(q4[:, 0], kv_pages, page_table, k_scale=k_scale, v_scale=v_scale, workers=workers)
+    st = _lib.decode_attn_paged_noalloc(ctypes.byref(d), q4.shape[1], _ptr(q), _ptr(kv_pages), _ptr(page_table),
+                                        _ptr(seq_lens), float(scale), _ptr(out), _ptr(lse), _stream(stream))
+    _check(st, "decode_attn_paged_noalloc")
+    return out, lse
+
+
 def decode_attn_mla_ws(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
                        scale: float, workspace: torch.Tensor, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
                        *, v_dim: int = 512, workers: int = 0, stream=None):
@@ -503,4 +530,5 @@ def timer_end():
 __all__ = ["timer_begin", "timer_end", "decode_attn_paged", "decode_attn_paged_rows", "decode_attn_mla",
            "decode_attn_mla_rows", "decode_attn_plan", "paged_kv_gather", "default_workers",
            "PagedDesc", "MLADesc", "DecodeAttnError", "LIB_PATH", "EXPORTS", "lib", "decode_kv_append", "decode_kv_append_mla",
-           "workspace_size", "decode_attn_paged_ws", "decode_attn_mla_ws", "validate_inputs"]
+           "workspace_size", "decode_attn_paged_ws", "decode_attn_mla_ws", "validate_inputs",
+           "decode_attn_paged_noalloc", "NOALLOC_SCRATCH_BYTES"]

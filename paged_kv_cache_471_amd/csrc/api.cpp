@@ -27,6 +27,16 @@ int hip_fail(hipError_t e) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+}  // namespace
+
+namespace da {
+// Lets other translation units of the library record a failed HIP call for
+// decode_attn_last_hip_error().
+int hip_failure(hipError_t e) { return hip_fail(e); }
+}  // namespace da
+
+namespace {
+
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ---------------------------------------------------------------- workspace
@@ -560,6 +570,7 @@ const char* decode_attn_status_str(int status) {
         case DA_ERR_WORKSPACE: return "workspace allocation failed";
         case DA_ERR_HIP: return "a HIP call failed";
         case DA_ERR_DATA: return "device data violates a precondition (length or page id out of range)";
+        case DA_ERR_SCRATCH: return "the call needs more workspace than the no-allocation entry point's static scratch holds";
         default: return "unknown status";
     }
 }
