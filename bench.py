@@ -43,25 +43,30 @@ KERNEL_SOURCES = ["paged_kv_cache_471_amd/csrc/gqa_mfma.hip", "paged_kv_cache_47
                   "paged_kv_cache_471_amd/csrc/da_common.h", "paged_kv_cache_471_amd/csrc/da_launch.h",
                   "paged_kv_cache_471_amd/csrc/da_plan.h"]
 PMC_FILE = os.path.join(ROOT, "profiles", "gqa_llama8b_pmc.md")
+# sources of the 128-head MLA kernel and its merge
+MLA_KERNEL_SOURCES = ["paged_kv_cache_471_amd/csrc/mla_wave.hip", "paged_kv_cache_471_amd/csrc/da_mla.h",
+                      "paged_kv_cache_471_amd/csrc/da_common.h", "paged_kv_cache_471_amd/csrc/da_launch.h",
+                      "paged_kv_cache_471_amd/csrc/da_plan.h"]
+MLA_PMC_FILE = os.path.join(ROOT, "profiles", "mla_pmc.md")
 
 
-def kernel_hash() -> str:
+def kernel_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (KERNEL_SOURCES if sources is None else sources):
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles():
-    """HBM bytes per launch of the GQA kernel from the committed counter summary,
-    or None when the summary is missing or was taken on a different kernel source."""
-    if not os.path.exists(PMC_FILE):
+def traffic_from_profiles(path=PMC_FILE, sources=None):
+    """HBM bytes per launch of a kernel from its committed counter summary, or
+    None when the summary is missing or was taken on a different kernel source."""
+    if not os.path.exists(path):
         return None
-    for line in open(PMC_FILE):
+    for line in open(path):
         if line.startswith("pmc: "):
             d = json.loads(line[5:])
-            if d.get("kernel_hash") != kernel_hash():
+            if d.get("kernel_hash") != kernel_hash(sources):
                 return None
             return d.get("traffic_bytes_per_launch")
     return None
@@ -137,26 +142,6 @@ class GqaRunner:
     def tokens(self):
         return int(self.case.seq_lens.astype("int64").sum())
 
-    def oracle_sample(self, budget_s):
-        """Time the float64 oracle on requests in order, passing over the batch
-        again and again, until the budget is spent."""
-        import numpy as np
-        import oracle
-        from workloads import accounting
-        c, cfg = self.case, self.cfg
-        B = len(c.seq_lens)
-        done = []
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget_s:
-            b = len(done) % B
-            oracle.paged_decode_attention(c.q, cfg.q_dtype, c.kv, cfg.kv_dtype, c.page_table, c.seq_lens,
-                                          cfg.page_size, c.scale, c.k_scale, c.v_scale, requests=[b])
-            done.append(b)
-        dt = time.perf_counter() - t0
-        lens = c.seq_lens[done]
-        by = accounting.gqa_bytes(lens, cfg.page_size, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.q_dtype,
-                                  cfg.kv_dtype)
-        return dict(seconds=dt, requests=len(done), tokens=int(lens.astype(np.int64).sum()), bytes=by)
 
 
 class MlaRunner:
@@ -332,11 +317,18 @@ CALIB = {
 }
 
 
+# bytes of K/V pages the calibration steps cycle through: twice the 256 MB
+# last-level cache and more, so that no step finds its pages left in it by
+# the steps before
+CALIB_ROTATE_BYTES = 640 * 10 ** 6
+
+
 class CalibRunner:
     """One decode step over a batch of stationary slot loads, on a K/V buffer
-    filled on the device (values do not change the time)."""
+    filled on the device (values do not change the time).  Consecutive steps
+    cycle through `sets` page tables over disjoint random pages of the buffer."""
 
-    def __init__(self, kind, lens, kv, gen):
+    def __init__(self, kind, lens, kv, gen, sets=1):
         import numpy as np
         import torch
         c = CALIB[kind]["shape"]
@@ -344,14 +336,20 @@ class CalibRunner:
         B = len(lens)
         P = c["page_size"]
         npg = (lens + P - 1) // P
+        need = int(npg.sum())
+        if sets * need > kv.shape[0]:
+            raise ValueError(f"{sets} page sets of {need} pages do not fit {kv.shape[0]} pages")
         width = int(npg.max())
-        table = np.full((B, width), -1, dtype=np.int32)
-        perm = np.random.default_rng(int(lens.sum())).permutation(int(npg.sum())).astype(np.int32)
+        perm = np.random.default_rng(int(lens.sum())).permutation(kv.shape[0]).astype(np.int32)
+        self.pts = []
         at = 0
-        for b in range(B):
-            table[b, :npg[b]] = perm[at:at + npg[b]]
-            at += int(npg[b])
-        self.pt = torch.from_numpy(table).cuda()
+        for _ in range(sets):
+            table = np.full((B, width), -1, dtype=np.int32)
+            for b in range(B):
+                table[b, :npg[b]] = perm[at:at + npg[b]]
+                at += int(npg[b])
+            self.pts.append(torch.from_numpy(table).cuda())
+        self.i = 0
         self.sl = torch.from_numpy(lens.astype(np.int32)).cuda()
         self.kv = kv
         if kind == "gqa":
@@ -364,10 +362,12 @@ class CalibRunner:
 
     def step(self):
         import paged_kv_cache_471_amd as da
+        pt = self.pts[self.i % len(self.pts)]
+        self.i += 1
         if self.kind == "gqa":
-            self.out, self.lse = da.decode_attn_paged(self.q, self.kv, self.pt, self.sl, self.scale, self.out, self.lse)
+            self.out, self.lse = da.decode_attn_paged(self.q, self.kv, pt, self.sl, self.scale, self.out, self.lse)
         else:
-            self.out, self.lse = da.decode_attn_mla(self.q, self.kv, self.pt, self.sl, self.scale, 512, self.out,
+            self.out, self.lse = da.decode_attn_mla(self.q, self.kv, pt, self.sl, self.scale, 512, self.out,
                                                     self.lse)
 
 
@@ -387,21 +387,25 @@ def calibrate_latency(kind, steps=20, warmup=5):
     loads = provision.slot_loads(Pt, Dt, step_at)
     sh = c["shape"]
     P = sh["page_size"]
-    pages = int(((loads + P - 1) // P).sum()) + 1
+    per_token = 2 * sh["kv_heads"] * sh["head_dim"] * 2 if kind == "gqa" else 576 * 2
+    plans = []
+    for B in c["slots"]:
+        lens = loads[:B].astype(np.int64)
+        need = int(((lens + P - 1) // P).sum())
+        plans.append((B, lens, need, max(2, math.ceil(CALIB_ROTATE_BYTES / (need * P * per_token)))))
+    pages = max(need * sets for _, _, need, sets in plans)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(wl.BASE_SEED + 7)
     if kind == "gqa":
         kv = torch.randn((pages, 2, sh["kv_heads"], P, sh["head_dim"]), generator=gen, device="cuda").to(torch.bfloat16)
-        per_token = 2 * sh["kv_heads"] * sh["head_dim"] * 2
     else:
         kv = (0.5 * torch.randn((pages, P, 576), generator=gen, device="cuda")).to(torch.bfloat16)
-        per_token = 576 * 2
     pts = []
-    for B in c["slots"]:
-        lens = loads[:B].astype(np.int64)
-        r = CalibRunner(kind, lens, kv, gen)
+    for B, lens, need, sets in plans:
+        r = CalibRunner(kind, lens, kv, gen, sets)
         ms, kms, _ = time_runner(r, steps, warmup, warm_s=0.1)
-        pts.append(dict(slots=B, T=int(lens.sum()), step_us=round(ms * 1e3, 2), kernel_us=round(kms * 1e3, 2)))
+        pts.append(dict(slots=B, T=int(lens.sum()), step_us=round(ms * 1e3, 2), kernel_us=round(kms * 1e3, 2),
+                        page_sets=sets, rotated_MB=round(sets * need * P * per_token / 1e6, 1)))
         del r
     T = [p["T"] for p in pts]
     ak, bk, r2k = provision.fit_latency(T, [p["kernel_us"] * 1e-6 for p in pts])
@@ -417,6 +421,91 @@ def calibrate_latency(kind, steps=20, warmup=5):
                    "effective_GBps": round(per_token / ak / 1e9, 1)},
         "step": {"alpha_ns_per_token": round(a_s * 1e9, 5), "beta_us": round(b_s * 1e6, 2), "r2": round(r2s, 5),
                  "effective_GBps": round(per_token / a_s / 1e9, 1)},
+    }
+
+
+def oracle_sample(cfg, case, budget_s, per_call=4):
+    """Time the float64 oracle on the workload's requests, `per_call` requests
+    per oracle call, taken in order and cycling over the batch, until the
+    budget is spent.  Returns seconds, requests, tokens and algorithmic bytes
+    of the requests done."""
+    import numpy as np
+    import oracle
+    import workloads as wl
+    from workloads import accounting
+    c = case
+    B = len(c.seq_lens)
+    done = []
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        reqs = [(len(done) + k) % B for k in range(min(per_call, B))]
+        if isinstance(cfg, wl.MLAConfig):
+            oracle.mla_decode_attention(c.q, c.kv, c.page_table, c.seq_lens, cfg.page_size, c.scale, cfg.v_dim,
+                                        requests=reqs)
+        else:
+            oracle.paged_decode_attention(c.q, cfg.q_dtype, c.kv, cfg.kv_dtype, c.page_table, c.seq_lens,
+                                          cfg.page_size, c.scale, c.k_scale, c.v_scale, requests=reqs)
+        done.extend(reqs)
+    dt = time.perf_counter() - t0
+    lens = c.seq_lens[done]
+    if isinstance(cfg, wl.MLAConfig):
+        by = accounting.mla_bytes(lens, cfg.page_size, c.q.shape[1], cfg.latent_dim, cfg.v_dim)
+    else:
+        by = accounting.gqa_bytes(lens, cfg.page_size, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.q_dtype,
+                                  cfg.kv_dtype)
+    return dict(seconds=dt, requests=len(done), tokens=int(lens.astype(np.int64).sum()), bytes=by)
+
+
+def host_cores():
+    """Threads the CPU baseline uses: the cores this process may run on,
+    capped by OMP_NUM_THREADS when the environment sets it."""
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return n
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(cases, headline, budget_s):
+    """The oracle, as it stands, on the host cores: a figure per workload
+    (the median of three samples for the tiny and the headline workload),
+    algorithmic GB/s and KV tokens/s."""
+    import statistics
+    import threadpoolctl
+    cores = host_cores()
+    per = {}
+    with threadpoolctl.threadpool_limits(cores):
+        for name, (cfg, case) in cases.items():
+            reps = 3 if name in ("tiny", headline) else 1
+            share = budget_s * (0.3 if name == headline else 0.15 if name != "tiny" else 0.05)
+            per_call = max(1, min(4, len(case.seq_lens) // 32))
+            runs = [oracle_sample(cfg, case, share / reps, per_call) for _ in range(reps)]
+            gbs = [r["bytes"] / r["seconds"] / 1e9 for r in runs]
+            med = sorted(range(reps), key=lambda i: gbs[i])[reps // 2]
+            r = runs[med]
+            per[name] = {"value": round(gbs[med], 4), "unit": "GB/s",
+                         "tokens_per_s": round(r["tokens"] / r["seconds"], 1),
+                         "samples": reps, "spread_GBps": [round(min(gbs), 4), round(max(gbs), 4)],
+                         "sample": f"{r['requests']} requests ({r['tokens']} tokens) in {r['seconds']:.2f} s"}
+    h = per[headline]
+    return {
+        "value": h["value"], "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "cpu_model": cpu_model(),
+        "sample": f"median of 3 samples of the {headline} workload's requests taken in order, cycling over the "
+                  f"batch ({h['sample']} for the median); float64 numpy with BLAS on "
+                  f"{cores} threads",
+        "tokens_per_s": h["tokens_per_s"],
+        "per_config": per,
     }
 
 
@@ -561,7 +650,8 @@ def main():
                     help="KV heads of a GQA headline workload instead of its own; 0 keeps the workload's")
     ap.add_argument("--secondary", default="tiny,skewed,mla,longfp8,llama8b-mtp2,mla-mtp2",
                     help="comma list of other workloads to report beside the headline ('' for none)")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for the CPU baseline")
+    ap.add_argument("--cpu-budget", type=float, default=30.0,
+                    help="seconds of oracle time for the CPU baseline, over all workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-latency-model", action="store_true", help="skip the t_A(T) calibration")
     ap.add_argument("--mode", choices=["bench", "copy", "step", "append", "calibrate"], default="bench",
@@ -615,7 +705,6 @@ def main():
 
     ms, kms, wall = time_runner(runner, args.steps, args.warmup, warm_s=SETTLE_S)
     per_call = step_percentiles(runner, max(100, args.steps))
-    headline_case = runner.case
     appends = {cfg.name: time_append(runner, args.steps, args.warmup, ms)}
     gbs = runner.bytes / (ms * 1e-3) / 1e9
     kern_gbs = runner.bytes / (kms * 1e-3) / 1e9 if kms else None
@@ -653,6 +742,7 @@ def main():
     }
 
     secondary = {}
+    host_cases = {cfg.name: (cfg, runner.case)}
     for name in [s for s in args.secondary.split(",") if s]:
         rows = 1
         if name in ROWS_WORKLOADS:
@@ -679,6 +769,21 @@ def main():
             entry["algorithmic_flops_per_step"] = runner2.flops
             entry["mfma_TFLOPs"] = round(runner2.flops / (sms * 1e-3) / 1e12, 1)
             entry["pct_mfma_bf16_peak"] = round(100 * runner2.flops / (sms * 1e-3) / MFMA_BF16_PEAK, 2)
+            if name == "mla" and skms:
+                kg = runner2.bytes / (skms * 1e-3) / 1e9
+                kf = runner2.flops / (skms * 1e-3)
+                entry["roofline"] = {
+                    "bound": "hbm", "kernel": "mla_wave_kernel",
+                    "achieved": round(kg, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(kg / HBM_PEAK_GBS, 4),
+                    "mfma": {"achieved_TFLOPs": round(kf / 1e12, 1), "peak_TFLOPs": MFMA_BF16_PEAK / 1e12,
+                             "frac": round(kf / MFMA_BF16_PEAK, 4)},
+                    "traffic": traffic_from_profiles(MLA_PMC_FILE, MLA_KERNEL_SOURCES),
+                    "kernel_ms": skms,
+                    "kernel_source_hash": kernel_hash(MLA_KERNEL_SOURCES),
+                }
+        if rows == 1:
+            host_cases[name] = (scfg, runner2.case)
         secondary[name] = entry
         if name in ("mla", "longfp8"):
             appends[name] = time_append(runner2, max(10, args.steps // 2), max(3, args.warmup // 2), sms)
@@ -697,22 +802,9 @@ def main():
         result["latency_model"] = {k: calibrate_latency(k) for k in CALIB}
 
     if not args.no_cpu_baseline:
-        import threadpoolctl
-        base = GqaRunner.__new__(GqaRunner)
-        base.cfg = cfg
-        base.case = headline_case
-        with threadpoolctl.threadpool_limits(1):
-            s = base.oracle_sample(args.cpu_budget)
-        result["cpu_baseline"] = {
-            "value": round(s["bytes"] / s["seconds"] / 1e9, 4),
-            "unit": "GB/s",
-            "cores": 1,
-            "kind": "oracle",
-            "sample": f"{s['requests']} requests of {cfg.name} taken in order, cycling over its "
-                      f"{len(base.case.seq_lens)} ({s['tokens']} tokens, {s['seconds']:.1f} s), float64 numpy, "
-                      f"BLAS limited to 1 thread",
-            "tokens_per_s": s["tokens"] / s["seconds"],
-        }
+        order = [n for n in ("tiny", "llama8b", "skewed", "mla", "longfp8") if n in host_cases]
+        order += [n for n in host_cases if n not in order]
+        result["cpu_baseline"] = cpu_baseline({n: host_cases[n] for n in order}, cfg.name, args.cpu_budget)
     print(json.dumps(result), flush=True)
 
 

@@ -52,9 +52,12 @@ def assert_close_gqa(case, out, lse, ref_out, ref_lse, requests=None, label=""):
     kvd = case.cfg.kv_dtype
     o = out_to_f64(out)
     l = lse.cpu().numpy().astype(np.float64)
+    # every request, checked against the oracle or not, gives finite outputs
+    # and a log-sum-exp that is finite or, for an empty history, -inf
+    assert np.all(np.isfinite(o)), f"{label}: non-finite output"
+    assert not np.any(np.isnan(l)) and not np.any(l == np.inf), f"{label}: NaN or +inf lse"
     rows = list(range(len(case.seq_lens))) if requests is None else list(requests)
     o, l, ro, rl = o[rows], l[rows], ref_out[rows], ref_lse[rows]
-    assert np.all(np.isfinite(o)), f"{label}: non-finite output"
     err = np.max(np.abs(o - ro)) if o.size else 0.0
     assert err <= TOL_OUT[kvd], f"{label}: max |out - oracle| = {err:.3e} > {TOL_OUT[kvd]}"
     fin = np.isfinite(rl)

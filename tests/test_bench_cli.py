@@ -32,7 +32,27 @@ def test_traffic_reported_only_for_the_profiled_kernel_source(monkeypatch):
     d = json.loads(line[5:])
     # the summary itself: each K/V byte read about once
     assert 1.0 <= d["traffic_bytes_per_launch"] / d["algorithmic_bytes_per_launch"] < 1.05
-    monkeypatch.setattr(bench, "kernel_hash", lambda: d["kernel_hash"])
+    monkeypatch.setattr(bench, "kernel_hash", lambda sources=None: d["kernel_hash"])
     assert bench.traffic_from_profiles() == d["traffic_bytes_per_launch"]
-    monkeypatch.setattr(bench, "kernel_hash", lambda: "0" * 16)
+    monkeypatch.setattr(bench, "kernel_hash", lambda sources=None: "0" * 16)
     assert bench.traffic_from_profiles() is None
+
+
+def test_cpu_baseline_uses_every_host_core_and_reports_each_workload():
+    """The CPU baseline runs the oracle with BLAS on all the cores the process
+    may use, names the CPU, and gives a figure per workload (median of three
+    samples for the tiny and the headline workload)."""
+    import workloads as wl
+    bench = _bench_module()
+    cores = bench.host_cores()
+    assert 1 <= cores <= len(os.sched_getaffinity(0))
+    tiny = wl.CONFIGS["tiny"]
+    small = wl.GQAConfig("small", 30, 3, 8, 2, 64, 16, wl.BF16, wl.BF16, "uniform:16:200")
+    cases = {"tiny": (tiny, wl.make_gqa_case(tiny)), "small": (small, wl.make_gqa_case(small))}
+    r = bench.cpu_baseline(cases, "small", 0.6)
+    assert r["cores"] == cores and r["kind"] == "oracle"
+    assert set(r["per_config"]) == {"tiny", "small"}
+    assert r["per_config"]["tiny"]["samples"] == 3 and r["per_config"]["small"]["samples"] == 3
+    assert r["value"] == r["per_config"]["small"]["value"] > 0
+    lo, hi = r["per_config"]["small"]["spread_GBps"]
+    assert lo <= r["value"] <= hi

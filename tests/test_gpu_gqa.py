@@ -202,31 +202,22 @@ def test_gather_bitwise(kd):
 
 # ----------------------------------------------------------------------------- full-size configurations
 
-def _sample_requests(case, n=6):
-    L = case.seq_lens
-    order = np.argsort(L)
-    picks = {int(order[0]), int(order[-1]), int(order[len(order) // 2])}
-    rng = np.random.default_rng(0)
-    picks.update(int(x) for x in rng.choice(len(L), size=min(n, len(L)), replace=False))
-    return sorted(picks)
-
-
 @pytest.mark.parametrize("name", ["llama8b", "skewed"])
-def test_full_size_bf16_sampled(name):
+def test_full_size_bf16_whole(name):
+    """The llama-8B-shaped batch and the skewed rollout-tail batch at full size
+    in the default launch: every output and log-sum-exp against the oracle."""
     case = wl.make_gqa_case(wl.CONFIGS[name])
     out, lse, _ = run(case)
-    reqs = _sample_requests(case)
-    if name == "skewed":
-        reqs = sorted(set(reqs) | set(int(i) for i in np.nonzero(case.seq_lens >= 32768)[0][:2]))
-    ro, rl = gqa_oracle(case, requests=reqs)
-    assert_close_gqa(case, out, lse, ro, rl, requests=reqs, label=name)
+    ro, rl = gqa_oracle(case)
+    assert_close_gqa(case, out, lse, ro, rl, label=name)
 
 
-def test_full_size_fp8_long_context_sampled():
+def test_full_size_fp8_long_context_whole():
+    """Both 131072-token fp8 requests at full size against the oracle."""
     case = wl.make_gqa_case(wl.LONGFP8)
     out, lse, _ = run(case)
-    ro, rl = gqa_oracle(case, requests=[1])
-    assert_close_gqa(case, out, lse, ro, rl, requests=[1], label="longfp8")
+    ro, rl = gqa_oracle(case)
+    assert_close_gqa(case, out, lse, ro, rl, label="longfp8")
 
 
 def test_fp8_long_context_reduced_whole():
