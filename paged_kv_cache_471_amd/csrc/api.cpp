@@ -441,9 +441,17 @@ int gqa_step(const da_paged_desc* d, int q_rows, const void* q, const void* kv_p
     // Streams split into about two pieces or fewer are merged by one
     // workgroup for all the heads of their group (fewer, fuller workgroups;
     // most of them return at once); more deeply split streams by one
-    // workgroup per head, so that their pieces spread over more lanes.
+    // workgroup per head, so that their pieces spread over more lanes, and
+    // streams of more than 16 pieces (few long requests) also by column
+    // chunks, down to 4 float4 columns per workgroup, so that each of a
+    // workgroup's threads folds about four pieces.
     const int pieces = ga.workers / (streams > 0 ? streams : 1);
     ma.heads_per_block = pieces <= 2 && members * d->head_dim <= 4 * 256 ? members : 1;
+    ma.col_chunks = 1;
+    if (ma.heads_per_block == 1 && pieces > 16) {
+        const int c4 = d->head_dim / 4;
+        while (ma.col_chunks * 4 < c4 && (c4 / ma.col_chunks) * pieces > 4 * 256) ma.col_chunks *= 2;
+    }
     ma.out_is_bf16 = d->q_dtype == DA_BF16;
     e = da::launch_merge(ma, streams, s);
     if (e != hipSuccess) return hip_fail(e);
@@ -550,6 +558,7 @@ int mla_step(const da_mla_desc* dd, int q_rows, const void* q, const void* kv_pa
     // thread, both loaded in one pass (measured: 20.4 us against 20.8 with
     // eight heads and four columns per thread)
     mg.heads_per_block = d->num_heads >= 4 ? 4 : d->num_heads;
+    mg.col_chunks = 1;
     mg.out_is_bf16 = 1;
     e = da::launch_merge(mg, d->batch, s);
     if (e != hipSuccess) return hip_fail(e);

@@ -82,8 +82,8 @@ struct MlaArgs {
 };
 
 // Log-sum-exp merge of the partial slots of split streams.  One workgroup per
-// (stream, group of heads_per_block heads); streams that are empty or were not
-// split return at once.
+// (stream, group of heads_per_block heads, 1/col_chunks of their columns);
+// streams that are empty or were not split return at once.
 struct MergeArgs {
     const int32_t* seq_lens;
     const int2* plan_info;
@@ -96,6 +96,7 @@ struct MergeArgs {
     int group;              // (row, head) slots per stream in the partials
     int dim;                // values per head
     int heads_per_block;    // divides group
+    int col_chunks;         // power of two dividing heads_per_block * dim / 4 (1: whole heads)
     int out_is_bf16;
     int rows;               // query rows per request; slot h is row h >> group_log2
     int group_log2;         // log2 of the query heads per stream

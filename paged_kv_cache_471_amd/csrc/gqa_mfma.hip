@@ -17,15 +17,32 @@
 //  * The result leaves lane (R, C) with tokens 4R..4R+3 of member C: the
 //    online softmax of a member runs over the four lanes of its column (two
 //    row swaps), in fp32.
-//  * Values: O[16 members][D] += P[16 members][16 tokens] . V[16 tokens][D]
-//    with v_mfma_f32_16x16x4_f32: fp32 weights and fp32 values, in four steps
-//    of four tokens.  Step i takes token 4R + i from lane row R, so each lane's
-//    own weights are its A operand and V loaded as tokens 4R + i, dims
-//    [C D/16, (C+1) D/16) is the B operand, with no data movement.
+//  * Values (bf16 and fp32 caches): O[16 members][D] += P[16 members][16
+//    tokens] . V[16 tokens][D] with v_mfma_f32_16x16x4_f32: fp32 weights and
+//    fp32 values, in four steps of four tokens.  Step i takes token 4R + i
+//    from lane row R, so each lane's own weights are its A operand and V
+//    loaded as tokens 4R + i, dims [C D/16, (C+1) D/16) is the B operand, with
+//    no data movement.
+//  * Values (fp8 cache): O^T[D][16 members] += V^T[D][16 tokens] . P^T[16
+//    tokens][16 members] with v_mfma_f32_16x16x16_bf16, D / 16 dim blocks.
+//    Each fp32 weight is split into two bf16 terms, hi = bf16(p) and lo =
+//    bf16(p - hi), so hi + lo equals p to within 2^-17 relative; both terms
+//    meet the same values (fp8 codes convert to bf16 exactly) in two
+//    products, exact in fp32 and accumulated in fp32.  The B operand of lane
+//    (R, C) is tokens 4R..4R+3 of member C: exactly the weights that lane
+//    holds after the softmax.  The A operand of dim block b is, for the
+//    lane's tokens 4R..4R+3, the code of dim C D/16 + b: byte b % 4 of word
+//    b / 4 of each token's loaded slice, gathered by byte permutes.  Row C of
+//    block b is thus dim C D/16 + b, and lane (R, C) ends holding member C's
+//    dims [4R D/16, 4R D/16 + 4 D/16): 16 dim blocks of 32-cycle fp32 steps
+//    per page become D/16 pairs of 8-cycle bf16 steps.
 //  * Members are the q_rows x (q_heads / kv_heads) (row, head) pairs of a KV
 //    head, up to 16; unused member columns carry zero queries and are never
 //    written.  Row r of a request sees positions up to len - q_rows + r.
 #include <hip/hip_ext.h>
+
+#include <type_traits>
+#include <utility>
 
 #include "da_common.h"
 #include "da_launch.h"
@@ -34,6 +51,16 @@
 
 namespace da {
 namespace {
+
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, i>) for i = 0 .. N-1
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 constexpr int kPage = 16;           // tokens per page (one MFMA tile)
 constexpr float kRaise = 8.0f;      // the running maximum moves only past this margin (base 2)
@@ -48,6 +75,27 @@ __device__ __forceinline__ floatx4_t mfma_s(bf16x8_t a, bf16x8_t b, floatx4_t c)
 }
 __device__ __forceinline__ floatx4_t mfma_v(float a, float b, floatx4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+typedef short short4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ floatx4_t mfma_v16(short4_t a, short4_t b, floatx4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ short4_t as_short4(uint32_t lo, uint32_t hi) {
+    return __builtin_bit_cast(short4_t, u32x2{lo, hi});
+}
+// two fp32 values -> packed bf16 pair, round to nearest even
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2_t));
+}
+// Byte k of each of four words, in order: v_perm_b32 selects bytes of the
+// 8-byte pair (first operand high, second low); selector 0x0c yields zero.
+template <int K>
+__device__ __forceinline__ uint32_t gather_byte(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+    constexpr uint32_t sel = uint32_t(K) | (uint32_t(4 + K) << 8) | (0x0cu << 16) | (0x0cu << 24);
+    const uint32_t t01 = __builtin_amdgcn_perm(w1, w0, sel);
+    const uint32_t t23 = __builtin_amdgcn_perm(w3, w2, sel);
+    return __builtin_amdgcn_perm(t23, t01, 0x05040100u);
 }
 
 // Pairwise max / sum over lanes (l, l ^ 16) and (l, l ^ 32): the four lanes
@@ -300,46 +348,90 @@ __global__ __launch_bounds__(kGqaBlock, MOcc<KV>::blocks_per_cu) void gqa_mfma_k
         l_run = __builtin_fmaf(l_run, alpha, psum);
         m_run = mn;
         if (__ballot(alpha != 1.0f) != 0ull) {
-            // accumulator rows are members 4R + x: their factors sit in columns 4R + x
-            float al[4];
+            if constexpr (KV == kFP8) {
+                // accumulator columns are members: this lane's own factor
 #pragma unroll
-            for (int x = 0; x < 4; ++x) al[x] = __shfl(alpha, 4 * R + x, 64);
+                for (int t = 0; t < DL; ++t)
 #pragma unroll
-            for (int t = 0; t < DL; ++t)
+                    for (int x = 0; x < 4; ++x) acc[t][x] *= alpha;
+            } else {
+                // accumulator rows are members 4R + x: their factors sit in columns 4R + x
+                float al[4];
 #pragma unroll
-                for (int x = 0; x < 4; ++x) acc[t][x] *= al[x];
+                for (int x = 0; x < 4; ++x) al[x] = __shfl(alpha, 4 * R + x, 64);
+#pragma unroll
+                for (int t = 0; t < DL; ++t)
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) acc[t][x] *= al[x];
+            }
         }
-        // ---- values: step i, token 4R + i
+        if constexpr (KV == kFP8) {
+            // ---- values: weights as bf16 hi + lo, the B operand (tokens 4R..4R+3 of member Cc)
+            const uint32_t h01 = bf16x2_rne(p[0], p[1]);
+            const uint32_t h23 = bf16x2_rne(p[2], p[3]);
+            const uint32_t l01 = bf16x2_rne(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
+            const uint32_t l23 = bf16x2_rne(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
+            const short4_t bh = as_short4(h01, h23);
+            const short4_t bl = as_short4(l01, l23);
+            auto block = [&](auto KB) {
+                constexpr int db = decltype(KB)::value;
+                constexpr int q = db >> 2;
+                const uint32_t codes = gather_byte<db & 3>(buf.v[0].w[q], buf.v[1].w[q], buf.v[2].w[q], buf.v[3].w[q]);
+                const short4_t av = as_short4(fp8x2_to_bf16x2<false>(codes), fp8x2_to_bf16x2<true>(codes));
+                acc[db] = mfma_v16(av, bh, acc[db]);
+                acc[db] = mfma_v16(av, bl, acc[db]);
+            };
+            static_for<DL>(block);
+        } else {
+            // ---- values: step i, token 4R + i
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float vf[DL];
-            if constexpr (KV == kBF16) {
+            for (int i = 0; i < 4; ++i) {
+                float vf[DL];
 #pragma unroll
                 for (int w = 0; w < VW; ++w) {
                     vf[2 * w] = bf16_lo(buf.v[i].w[w]);
                     vf[2 * w + 1] = bf16_hi(buf.v[i].w[w]);
                 }
-            } else {
 #pragma unroll
-                for (int w = 0; w < VW; ++w) {
-                    const floatx2_t lo = fp8x2_to_f32x2<false>(buf.v[i].w[w]);
-                    const floatx2_t hi = fp8x2_to_f32x2<true>(buf.v[i].w[w]);
-                    vf[4 * w] = lo.x; vf[4 * w + 1] = lo.y;
-                    vf[4 * w + 2] = hi.x; vf[4 * w + 3] = hi.y;
-                }
+                for (int t = 0; t < DL; ++t) acc[t] = mfma_v(p[i], vf[t], acc[t]);
             }
-#pragma unroll
-            for (int t = 0; t < DL; ++t) acc[t] = mfma_v(p[i], vf[t], acc[t]);
         }
     };
 
-    // write the piece: member 4R + x, dims [Cc DL, Cc DL + DL)
+    // write the piece: member 4R + x, dims [Cc DL, Cc DL + DL); with an fp8
+    // cache member Cc, dims [4R DL, 4R DL + 4 DL) (dim 4R DL + DL x + t in acc[t][x])
     auto finalize = [&](bool whole, int slot) {
         const bool seen = l_run > 0.0f;
         const float inv_col = seen ? vsc / l_run : 0.0f;
         const float lse2 = seen ? m_run + __builtin_log2f(l_run) : -__builtin_inff();
+        if constexpr (KV == kFP8) {
+            if (mlive) {
+                const int d0 = 4 * R * DL;
+                if (whole) {
+                    const int64_t row = (static_cast<int64_t>(cc.b) * NR + mrow) * Hq + (cc.j << RG) + (Cc & (G - 1));
+                    uint16_t* dst = static_cast<uint16_t*>(a.out) + row * D + d0;
+                    uint32_t packed[2 * DL];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
+                    for (int e = 0; e < 2 * DL; ++e)
+                        packed[e] = bf16x2_rne(acc[(2 * e) % DL][(2 * e) / DL] * inv_col,
+                                               acc[(2 * e + 1) % DL][(2 * e + 1) / DL] * inv_col);
+#pragma unroll
+                    for (int e = 0; e < DL / 2; ++e)
+                        reinterpret_cast<u32x4*>(dst)[e] = u32x4{packed[4 * e], packed[4 * e + 1], packed[4 * e + 2],
+                                                                packed[4 * e + 3]};
+                } else {
+                    float* dst = a.o_part + (static_cast<int64_t>(slot) * MT + Cc) * D + d0;
+#pragma unroll
+                    for (int e = 0; e < DL; ++e)
+                        reinterpret_cast<floatx4_t*>(dst)[e] = floatx4_t{
+                            acc[(4 * e) % DL][(4 * e) / DL] * inv_col, acc[(4 * e + 1) % DL][(4 * e + 1) / DL] * inv_col,
+                            acc[(4 * e + 2) % DL][(4 * e + 2) / DL] * inv_col,
+                            acc[(4 * e + 3) % DL][(4 * e + 3) / DL] * inv_col};
+                }
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < (KV == kFP8 ? 0 : 4); ++x) {
             const int mem = 4 * R + x;
             const float inv = __shfl(inv_col, mem, 64);
             if ((mem >> RG) >= NR) continue;

@@ -8,9 +8,11 @@
 // Layouts of Attention with Seamless Handoff for LLM Serving", §3,
 // Computation; §6 on context-parallel attention that splits one context).
 //
-// One 256-thread workgroup per (stream, group of heads).  Work spreads over
-// the whole GPU, so a stream split over many workers (a long request on few
-// streams) is merged with many loads in flight rather than by one worker.
+// One 256-thread workgroup per (stream, group of heads, chunk of their float4
+// columns).  Work spreads over the whole GPU, so a stream split over many
+// workers (a long request on few streams) is merged with many loads in
+// flight rather than by one worker: narrower column chunks leave more of a
+// workgroup's threads to the pieces, each folding a few of them.
 // Every reduction runs in a fixed order, so results are deterministic.
 // With several query rows per request a piece can hold no position that a row
 // sees; such a piece carries log-sum-exp -inf and weighs nothing, and a row
@@ -102,8 +104,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     const int t = threadIdx.x;
     const int nh = a.heads_per_block;
     const int per_stream = a.group / nh;
-    const int s = blockIdx.x / per_stream;
-    const int h0 = (blockIdx.x % per_stream) * nh;
+    const int chunk = blockIdx.x % a.col_chunks;
+    const int blk = blockIdx.x / a.col_chunks;
+    const int s = blk / per_stream;
+    const int h0 = (blk % per_stream) * nh;
     if ((h0 >> a.group_log2) >= a.rows) return;          // members that only pad the group
     const int b = s / a.units;
     const int j = s % a.units;
@@ -123,19 +127,20 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     // Thread (q, c): float4 column c of [nh][D], pieces i = q, q + PL, ...  Each
     // thread folds its pieces with a running maximum, then the PL piece lanes
     // of a column are folded in a fixed order; one round trip to memory.
-    const int C4 = nh * D / 4;
+    const int C4 = nh * D / 4 / a.col_chunks;             // float4 columns of this workgroup
+    const int cbase = chunk * C4;
     const int cols = C4 < kThreads ? C4 : kThreads;       // columns handled at once
     const int PL = kThreads / cols;                       // piece lanes per column
     const int q = t / cols;
     const int heads = a.units << a.group_log2;            // query heads per row
     const int gmask = (1 << a.group_log2) - 1;
     const int d4_log2 = __builtin_ctz(static_cast<unsigned>(D)) - 2;   // D is a power of two
-    if (C4 == 2 * kThreads) {
+    if (C4 == 2 * kThreads && a.col_chunks == 1) {
         fold_columns<2>(a, t, b, j, h0, n, gf, start, W, A, heads, gmask, d4_log2);
         return;
     }
     for (int c0 = 0; c0 < C4; c0 += cols) {
-        const int c = c0 + t % cols;
+        const int c = cbase + c0 + t % cols;
         const int h = c >> d4_log2;
         const int cc = c - (h << d4_log2);                // float4 column within the head
         const int slot_h = h0 + h;                        // (row, head) slot of the stream
@@ -159,13 +164,15 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
             m = mn;
         }
         if (PL > 1) {
+            // pairwise tree over the piece lanes: in each round lane q < half
+            // folds lane q + half, in a fixed order
             part[t] = acc;
             pm[t] = m;
             pz[t] = z;
             __syncthreads();
-            if (q == 0) {
-                for (int pr = 1; pr < PL; ++pr) {
-                    const int u = t + pr * cols;
+            for (int half = PL / 2; half >= 1; half >>= 1) {
+                if (q < half) {
+                    const int u = t + half * cols;
                     const float mo = pm[u];
                     const float mn = fmaxf(fmaxf(m, mo), kFloor);
                     const float fs = __builtin_amdgcn_exp2f(m - mn);
@@ -177,9 +184,12 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
                     acc.z = acc.z * fs + o.z * fo;
                     acc.w = acc.w * fs + o.w * fo;
                     m = mn;
+                    part[t] = acc;
+                    pm[t] = m;
+                    pz[t] = z;
                 }
+                __syncthreads();
             }
-            __syncthreads();
         }
         if (q == 0 && r < a.rows) {
             const float inv = z > 0.0f ? 1.0f / z : 0.0f;
@@ -200,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, int streams, hipStream_t s) {
-    const int grid = streams * (a.group / a.heads_per_block);
+    const int grid = streams * (a.group / a.heads_per_block) * a.col_chunks;
     hipLaunchKernelGGL(merge_kernel, dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
