@@ -77,6 +77,8 @@ def gqa_kernel_name(cfg, rows: int = 1) -> str:
     import workloads as wl
     members = rows * cfg.q_heads // cfg.kv_heads
     mfma = cfg.q_dtype == wl.BF16 and 4 <= members <= 16
+    if os.environ.get("DA_GQA_VECTOR") == "1" and members <= 8:
+        mfma = False
     return "gqa_mfma_kernel" if mfma else "gqa_attn_kernel"
 
 
@@ -658,7 +660,11 @@ def main():
                     help="copy: time a plain device copy; step: run the headline step only; append: run the "
                          "workload's KV append only (both for profilers)")
     ap.add_argument("--copy-mb", type=int, default=1024)
+    ap.add_argument("--gqa-kernel", choices=["auto", "vector"], default="auto",
+                    help="vector: run GQA groups of up to 8 members on the vector kernel (profiling)")
     args = ap.parse_args()
+    if args.gqa_kernel == "vector":
+        os.environ["DA_GQA_VECTOR"] = "1"      # read by the library at its first GQA call
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not offered "

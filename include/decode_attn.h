@@ -369,6 +369,13 @@ int decode_attn_default_workers(const da_paged_desc* gqa_or_null, const da_mla_d
  * the recorded events, returns the summed kernel time in milliseconds and the
  * number of timed launches, and releases the events.
  */
+/*
+ * Kernel choice for profiling: with DA_GQA_VECTOR=1 in the environment when
+ * the library first runs a GQA call, every group of up to 8 (row, head)
+ * members takes the vector kernel, including the 4 to 8 member bf16 and fp8
+ * groups that otherwise run on the matrix cores.  Results stay within the
+ * same bounds; not for production use.
+ */
 int decode_attn_timer_begin(int32_t max_launches);
 int decode_attn_timer_end(double* total_ms, int32_t* launches);
 

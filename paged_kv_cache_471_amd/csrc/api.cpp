@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -264,8 +265,21 @@ int check_paged(const da_paged_desc* d) {
 // vector kernel is bound by its ALUs, and at 4 the matrix-core kernel still
 // measured 2-3 % faster (less vector work beside the loads).  Smaller groups
 // and fp32 queries run on the vector kernel (gqa.hip).
+//
+// Profiling aid: DA_GQA_VECTOR=1 in the environment (read once per process)
+// sends every group the vector kernel can take (up to 8 members) to it, so
+// that both kernels can be measured on the same workload.
+bool vector_forced() {
+    static const bool forced = [] {
+        const char* e = std::getenv("DA_GQA_VECTOR");
+        return e != nullptr && e[0] == '1' && e[1] == '\0';
+    }();
+    return forced;
+}
+
 bool gqa_uses_mfma(const da_paged_desc* d, int q_rows) {
     const int want = q_rows * (d->num_q_heads / d->num_kv_heads);
+    if (want <= 8 && vector_forced()) return false;
     return d->q_dtype == DA_BF16 && (d->kv_dtype == DA_BF16 || d->kv_dtype == DA_FP8_E4M3) && want >= 4 &&
            want <= 16;
 }
