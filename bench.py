@@ -72,6 +72,18 @@ def traffic_from_profiles(path=PMC_FILE, sources=None):
     return None
 
 
+def counters_from_profiles(path, sources):
+    """The machine-readable `sq:` line of a committed SQ-counter summary, or
+    None when it is missing or was taken on a different kernel source."""
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("sq: "):
+            d = json.loads(line[4:])
+            return d if d.get("kernel_hash") == kernel_hash(sources) else None
+    return None
+
+
 def gqa_kernel_name(cfg, rows: int = 1) -> str:
     """The GQA attention kernel the library runs for this head shape."""
     import workloads as wl
@@ -785,6 +797,8 @@ def main():
                     "mfma": {"achieved_TFLOPs": round(kf / 1e12, 1), "peak_TFLOPs": MFMA_BF16_PEAK / 1e12,
                              "frac": round(kf / MFMA_BF16_PEAK, 4)},
                     "traffic": traffic_from_profiles(MLA_PMC_FILE, MLA_KERNEL_SOURCES),
+                    "counters": counters_from_profiles(os.path.join(ROOT, "profiles", "mla_sq_counters.md"),
+                                                       MLA_KERNEL_SOURCES),
                     "kernel_ms": skms,
                     "kernel_source_hash": kernel_hash(MLA_KERNEL_SOURCES),
                 }

@@ -56,3 +56,17 @@ def test_cpu_baseline_uses_every_host_core_and_reports_each_workload():
     assert r["value"] == r["per_config"]["small"]["value"] > 0
     lo, hi = r["per_config"]["small"]["spread_GBps"]
     assert lo <= r["value"] <= hi
+
+
+def test_mla_counters_reported_only_for_the_profiled_kernel_source(monkeypatch):
+    """The MLA roofline block carries traffic and SQ-counter fractions from the
+    committed summaries only while the MLA kernel sources hash to the value
+    recorded with them."""
+    bench = _bench_module()
+    sq = os.path.join(bench.ROOT, "profiles", "mla_sq_counters.md")
+    d = bench.counters_from_profiles(sq, bench.MLA_KERNEL_SOURCES)
+    assert d is not None and 0.0 < d["mfma_busy_frac"] < 1.0
+    assert bench.traffic_from_profiles(bench.MLA_PMC_FILE, bench.MLA_KERNEL_SOURCES) is not None
+    monkeypatch.setattr(bench, "kernel_hash", lambda sources=None: "0" * 16)
+    assert bench.counters_from_profiles(sq, bench.MLA_KERNEL_SOURCES) is None
+    assert bench.traffic_from_profiles(bench.MLA_PMC_FILE, bench.MLA_KERNEL_SOURCES) is None
