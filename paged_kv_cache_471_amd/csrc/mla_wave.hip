@@ -220,7 +220,8 @@ __global__ __launch_bounds__(kBlock, 1) void mla_wave_kernel(MlaArgs a) {
     auto v_doff = [](int db) { return 16 * (256 * (db >> 2) + 16 * (db & 3)); };
 
     bf16x8_t qreg[kNHB][kKB];
-    float m_run[kNHB], l_run[kNHB];
+    float m_run[kNHB];
+    float l_run[kNHB];       // this lane's part of each head's running sum (its four lanes add up to it)
     floatx4_t acc[kNHB][kVB];
 
     auto load_q = [&](int b) {
@@ -396,55 +397,78 @@ __global__ __launch_bounds__(kBlock, 1) void mla_wave_kernel(MlaArgs a) {
             if (more) chunk_issued();
 
             // ---- online softmax of this wave's 32 heads, entirely in registers:
-            //      head 16 hb + l16 spreads over lanes l16 + 16 q (q < 4)
+            //      head 16 hb + l16 spreads over lanes l16 + 16 q (q < 4).  The
+            //      running maximum is raised only when some score exceeds it by
+            //      more than kRaise, which one ballot over the lanes' own maxima
+            //      detects; only then are a head's four lanes reduced to its
+            //      chunk maximum.  Otherwise the weights take the running maximum
+            //      as it stands, and each lane keeps its own part of the running
+            //      sum, which is reduced over the four lanes when it is needed.
             bf16x8_t pop[kNHB];
-            float psums[kNHB], m_next[kNHB];
+            float sv[kNHB][8], lmax[kNHB];
 #pragma unroll
             for (int hb = 0; hb < kNHB; ++hb) {
-                float sv[8];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    sv[r] = sacc[0][hb][r] * a.scale_log2;
-                    sv[4 + r] = sacc[1][hb][r] * a.scale_log2;
+                    sv[hb][r] = sacc[0][hb][r] * a.scale_log2;
+                    sv[hb][4 + r] = sacc[1][hb][r] * a.scale_log2;
                 }
                 if (nvalid < kMlaChunk) {                           // wave-uniform
                     const int nv = nvalid - 4 * (fresh_lane() >> 4);   // live tokens from this lane's rows
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        if (r >= nv) sv[r] = -__builtin_inff();
-                        if (16 + r >= nv) sv[4 + r] = -__builtin_inff();
+                        if (r >= nv) sv[hb][r] = -__builtin_inff();
+                        if (16 + r >= nv) sv[hb][4 + r] = -__builtin_inff();
                     }
                 }
-                float cmax = sv[0];
+                lmax[hb] = sv[hb][0];
 #pragma unroll
-                for (int r = 1; r < 8; ++r) cmax = fmaxf(cmax, sv[r]);
-                cmax = max_xor32(max_xor16(cmax));
-                const float m_new = cmax > m_run[hb] + kRaise ? cmax : m_run[hb];
-                float p[8], psum = 0.0f;
+                for (int r = 1; r < 8; ++r) lmax[hb] = fmaxf(lmax[hb], sv[hb][r]);
+            }
+            bool raise = false;
+#pragma unroll
+            for (int hb = 0; hb < kNHB; ++hb) raise = raise || lmax[hb] > m_run[hb] + kRaise;
+            float m_next[kNHB];
+            bool restart = first_chunk;
+            if (__ballot(raise) != 0ull) {                          // wave-uniform, rare after a piece's first chunk
+#pragma unroll
+                for (int hb = 0; hb < kNHB; ++hb) {
+                    const float cmax = max_xor32(max_xor16(lmax[hb]));
+                    m_next[hb] = cmax > m_run[hb] + kRaise ? cmax : m_run[hb];
+                }
+                restart = restart || __ballot(m_next[0] != m_run[0] || m_next[kNHB - 1] != m_run[kNHB - 1]) != 0ull;
+            } else {
+#pragma unroll
+                for (int hb = 0; hb < kNHB; ++hb) m_next[hb] = m_run[hb];
+            }
+            float psum[kNHB];
+#pragma unroll
+            for (int hb = 0; hb < kNHB; ++hb) {
+                float p[8];
+                psum[hb] = 0.0f;
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
-                    p[r] = __builtin_amdgcn_exp2f(sv[r] - m_new);
-                    psum += p[r];
+                    p[r] = __builtin_amdgcn_exp2f(sv[hb][r] - m_next[hb]);
+                    psum[hb] += p[r];
                 }
                 const uint32_t pk[4] = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                                         pack_bf16x2(p[6], p[7])};
                 pop[hb] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-                psum = sum_xor32(sum_xor16(psum));
-                psums[hb] = psum;
-                m_next[hb] = m_new;
             }
             // A head's maximum moved (rare): rather than rescaling the
             // accumulators, which vector instructions never touch, fold them
             // (weights relative to the old maxima) into the piece's slot and
             // start a new accumulation from zero with this chunk.
-            const bool restart = first_chunk || __ballot(m_next[0] != m_run[0] || m_next[kNHB - 1] != m_run[kNHB - 1]) != 0ull;
             if (restart && !first_chunk) {
-                fold_into_slot(m_run, l_run);
+                float l_tot[kNHB];
+#pragma unroll
+                for (int hb = 0; hb < kNHB; ++hb) l_tot[hb] = sum_xor32(sum_xor16(l_run[hb]));
+                fold_into_slot(m_run, l_tot);
                 folded = true;
             }
 #pragma unroll
             for (int hb = 0; hb < kNHB; ++hb) {
-                l_run[hb] = restart ? psums[hb] : l_run[hb] + psums[hb];
+                l_run[hb] = restart ? psum[hb] : l_run[hb] + psum[hb];
                 m_run[hb] = m_next[hb];
             }
 
@@ -509,10 +533,13 @@ __global__ __launch_bounds__(kBlock, 1) void mla_wave_kernel(MlaArgs a) {
 #pragma unroll
             for (int hb = 0; hb < kNHB; ++hb) {
                 m_seg[hb] = m_run[hb];
-                l_seg[hb] = l_run[hb];
+                l_seg[hb] = sum_xor32(sum_xor16(l_run[hb]));
             }
         } else {
-            fold_into_slot(m_run, l_run);
+            float l_tot[kNHB];
+#pragma unroll
+            for (int hb = 0; hb < kNHB; ++hb) l_tot[hb] = sum_xor32(sum_xor16(l_run[hb]));
+            fold_into_slot(m_run, l_tot);
         }
         {
             const int le = fresh_lane();
