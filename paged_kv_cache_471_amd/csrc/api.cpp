@@ -460,11 +460,11 @@ int gqa_step(const da_paged_desc* d, int q_rows, const void* q, const void* kv_p
     // chunks, down to 4 float4 columns per workgroup, so that each of a
     // workgroup's threads folds about four pieces.
     const int pieces = ga.workers / (streams > 0 ? streams : 1);
-    ma.heads_per_block = pieces <= 2 && members * d->head_dim <= 4 * 256 ? members : 1;
+    ma.heads_per_block = pieces <= 2 && members * d->head_dim <= 4 * 128 ? members : 1;
     ma.col_chunks = 1;
     if (ma.heads_per_block == 1 && pieces > 16) {
         const int c4 = d->head_dim / 4;
-        while (ma.col_chunks * 4 < c4 && (c4 / ma.col_chunks) * pieces > 4 * 256) ma.col_chunks *= 2;
+        while (ma.col_chunks * 4 < c4 && (c4 / ma.col_chunks) * pieces > 4 * 128) ma.col_chunks *= 2;
     }
     ma.out_is_bf16 = d->q_dtype == DA_BF16;
     e = da::launch_merge(ma, streams, s);

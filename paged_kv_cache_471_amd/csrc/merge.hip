@@ -8,7 +8,7 @@
 // Layouts of Attention with Seamless Handoff for LLM Serving", §3,
 // Computation; §6 on context-parallel attention that splits one context).
 //
-// One 256-thread workgroup per (stream, group of heads, chunk of their float4
+// One 128-thread workgroup per (stream, group of heads, chunk of their float4
 // columns).  Work spreads over the whole GPU, so a stream split over many
 // workers (a long request on few streams) is merged with many loads in
 // flight rather than by one worker: narrower column chunks leave more of a
@@ -27,7 +27,7 @@
 namespace da {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 128;
 constexpr float kFloor = -3.0e38f;
 
 // NC float4 columns per thread (t, t + kThreads, ...; MLA's 512-value heads):
@@ -135,6 +135,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     const int heads = a.units << a.group_log2;            // query heads per row
     const int gmask = (1 << a.group_log2) - 1;
     const int d4_log2 = __builtin_ctz(static_cast<unsigned>(D)) - 2;   // D is a power of two
+    if (C4 == 4 * kThreads && a.col_chunks == 1) {
+        fold_columns<4>(a, t, b, j, h0, n, gf, start, W, A, heads, gmask, d4_log2);
+        return;
+    }
     if (C4 == 2 * kThreads && a.col_chunks == 1) {
         fold_columns<2>(a, t, b, j, h0, n, gf, start, W, A, heads, gmask, d4_log2);
         return;
