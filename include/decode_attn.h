@@ -81,7 +81,14 @@ extern "C" {
  *
  * kv_pages layout: [num_pages][2][num_kv_heads][page_size][head_dim] of
  * kv_dtype; index 0 of the second axis holds keys, 1 values.  Each
- * (page, K|V, head) block is page_size * head_dim contiguous elements.
+ * (page, K|V, head) block is page_size * head_dim contiguous elements,
+ * row-major [slot][dim], except the V blocks of an fp8 cache: those are kept
+ * in tiles of 16 slots (16 * head_dim bytes each, in slot order), and within
+ * a tile, with DL = head_dim / 16, the code of slot s (0..15) and dim d sits
+ * at byte 1024 * ((d % DL) / 4) + 256 * (s / 4) + 16 * (d / DL) + 4 * (d % 4)
+ * + s % 4, so that the codes of four consecutive slots for one dim are
+ * adjacent (the layout the matrix-core kernel reads with 16-byte loads).
+ * decode_kv_append writes and paged_kv_gather reads this layout.
  * q: [batch][num_q_heads][head_dim] of q_dtype; out: same shape and dtype.
  * lse: [batch][num_q_heads] fp32.  page_table: int32 [batch][max_pages_per_seq].
  * seq_lens: int32 [batch].
@@ -94,9 +101,11 @@ extern "C" {
  *
  * Kernels: bf16 queries with 4 to 16 query heads (or, with several query
  * rows, row x head pairs) per KV head run on the matrix cores (scores and
- * values as MFMA products, softmax weights kept in fp32); fp32 queries and
- * groups of 1 or 2 on the vector ALUs.  Both give the same semantics and the
- * same tolerances; kv_pages must be 16-byte aligned on the matrix-core path.
+ * values as MFMA products, softmax weights kept in fp32, split into two bf16
+ * terms for the fp8 value product); fp8 caches run there for every group
+ * size; fp32 queries and bf16 groups of 1 or 2 on the vector ALUs.  Both
+ * give the same semantics and the same tolerances; kv_pages must be 16-byte
+ * aligned on the matrix-core path.
  *
  * workers: number of workers, 0 selects the library default (one per resident
  * wavefront).  A worker is one wavefront that processes one contiguous share
@@ -372,9 +381,10 @@ int decode_attn_default_workers(const da_paged_desc* gqa_or_null, const da_mla_d
 /*
  * Kernel choice for profiling: with DA_GQA_VECTOR=1 in the environment when
  * the library first runs a GQA call, every group of up to 8 (row, head)
- * members takes the vector kernel, including the 4 to 8 member bf16 and fp8
- * groups that otherwise run on the matrix cores.  Results stay within the
- * same bounds; not for production use.
+ * members takes the vector kernel, including the 4 to 8 member bf16 groups
+ * that otherwise run on the matrix cores (fp8 caches always run on the
+ * matrix cores).  Results stay within the same bounds; not for production
+ * use.
  */
 int decode_attn_timer_begin(int32_t max_launches);
 int decode_attn_timer_end(double* total_ms, int32_t* launches);

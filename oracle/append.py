@@ -23,6 +23,7 @@ from __future__ import annotations
 
 import numpy as np
 
+from .attention import fp8_v_byte
 from .formats import F32, BF16, FP8, fp8_e4m3fn_table
 
 _TABLE = fp8_e4m3fn_table()
@@ -93,7 +94,15 @@ def kv_append(kv_pages, kv_dtype: int, k_new, v_new, new_dtype: int, page_table,
             ks = None if k_scale is None else k_scale[j]
             vs = None if v_scale is None else v_scale[j]
             kv[pg, 0, j, r, :] = _convert(k_new[b, j], new_dtype, kv_dtype, ks)
-            kv[pg, 1, j, r, :] = _convert(v_new[b, j], new_dtype, kv_dtype, vs)
+            v = _convert(v_new[b, j], new_dtype, kv_dtype, vs)
+            if kv_dtype == FP8:
+                # V blocks of an fp8 cache are tiled (attention.py, reading 8)
+                D = kv.shape[4]
+                block = kv[pg, 1, j].reshape(-1)
+                block[fp8_v_byte(r, np.arange(D, dtype=np.int64), D)] = v
+                kv[pg, 1, j] = block.reshape(kv.shape[3], D)
+            else:
+                kv[pg, 1, j, r, :] = v
     return kv
 
 

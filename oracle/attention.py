@@ -29,7 +29,14 @@ Readings where the pages are silent (each is a choice, stated once here):
 7. Slots of the last page at or past L are not history; their contents
    (possibly NaN) never reach the result.
 8. GQA pages are laid out [num_pages][2 (K, V)][Hkv][P][D]; MLA pages
-   [num_pages][P][576].  Only gather_history knows the layout.
+   [num_pages][P][576].  Only gather_history knows the layout.  In an fp8
+   cache (uint8 storage) each V block [P][D] is kept in 16-token tiles;
+   with DL = D / 16, token s of the tile (s = slot % 16) and dim d sit at byte
+       1024 * ((d mod DL) div 4) + 256 * (s div 4) + 16 * (d div DL)
+       + 4 * (d mod 4) + (s mod 4)
+   of the tile, the tile at byte 16 * D * (slot div 16) of the block: the
+   codes of four consecutive tokens for one dim are adjacent.  K blocks and
+   bf16 / fp32 caches are row-major [P][D].
 9. fp8 K/V dequantise as e4m3fn(code) * scale[j], one fp32 scale per KV head
    for K and one for V (SPLASH, App. B.1 mentions the scales traveling with
    the FP8 cache; the granularity is a reading).
@@ -44,6 +51,17 @@ import numpy as np
 from .formats import decode_storage, FP8
 
 
+def fp8_v_byte(slot, d, head_dim: int):
+    """Byte of (slot, dim d) within an fp8 V block of one (page, KV head)
+    (reading 8).  Works elementwise on integer arrays."""
+    if head_dim % 64 != 0:
+        raise ValueError("the tiled fp8 V layout is defined for head_dim a multiple of 64")
+    DL = head_dim // 16
+    tile, s = slot // 16, slot % 16
+    within = 1024 * ((d % DL) // 4) + 256 * (s // 4) + 16 * (d // DL) + 4 * (d % 4) + (s % 4)
+    return 16 * head_dim * tile + within
+
+
 def gather_history(kv_pages: np.ndarray, page_table: np.ndarray, b: int, length: int,
                    page_size: int, mla: bool = False):
     """Explicitly gather request b's first ``length`` tokens, in logical order, still
@@ -53,7 +71,17 @@ def gather_history(kv_pages: np.ndarray, page_table: np.ndarray, b: int, length:
     r = t % page_size
     if mla:
         return kv_pages[pg, r, :]
-    return kv_pages[pg, 0, :, r, :], kv_pages[pg, 1, :, r, :]
+    k = kv_pages[pg, 0, :, r, :]
+    if kv_pages.dtype != np.uint8:
+        return k, kv_pages[pg, 1, :, r, :]
+    # fp8: V blocks are tiled (reading 8); pick each (token, dim) byte
+    Hkv, D = kv_pages.shape[2], kv_pages.shape[4]
+    if page_size % 16 != 0:
+        raise ValueError("the tiled fp8 V layout is defined for pages of a multiple of 16 tokens")
+    blocks = kv_pages[pg, 1].reshape(length, Hkv, page_size * D)          # [L][Hkv][P*D]
+    byte = fp8_v_byte(r[:, None], np.arange(D, dtype=np.int64)[None, :], D)  # [L][D]
+    v = np.take_along_axis(blocks, np.broadcast_to(byte[:, None, :], (length, Hkv, D)), axis=2)
+    return k, v
 
 
 def dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):

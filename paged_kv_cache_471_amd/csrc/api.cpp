@@ -263,8 +263,9 @@ int check_paged(const da_paged_desc* d) {
 // Groups of 4 to 16 (row, head) members with bf16 queries run on the
 // matrix-core kernel (gqa_mfma.hip): from 8 query heads per K/V page up the
 // vector kernel is bound by its ALUs, and at 4 the matrix-core kernel still
-// measured 2-3 % faster (less vector work beside the loads).  Smaller groups
-// and fp32 queries run on the vector kernel (gqa.hip).
+// measured 1-3 % faster (less vector work beside the loads).  Smaller bf16
+// groups and fp32 queries run on the vector kernel (gqa.hip); fp8 caches run
+// on the matrix-core kernel for every group size.
 //
 // Profiling aid: DA_GQA_VECTOR=1 in the environment (read once per process)
 // sends every group the vector kernel can take (up to 8 members) to it, so
@@ -279,6 +280,9 @@ bool vector_forced() {
 
 bool gqa_uses_mfma(const da_paged_desc* d, int q_rows) {
     const int want = q_rows * (d->num_q_heads / d->num_kv_heads);
+    // fp8 caches keep their V blocks in tiles that only the matrix-core
+    // kernel reads: every group size runs there
+    if (d->kv_dtype == DA_FP8_E4M3) return d->q_dtype == DA_BF16 && want <= 16;
     if (want <= 8 && vector_forced()) return false;
     return d->q_dtype == DA_BF16 && (d->kv_dtype == DA_BF16 || d->kv_dtype == DA_FP8_E4M3) && want >= 4 &&
            want <= 16;

@@ -9,8 +9,9 @@
 // Token t of request b sits in page page_table[b][t / P], slot t % P; a
 // negative position skips the request.  GQA: one workgroup per (request, K|V)
 // writes Hkv * D values, four per thread (16-byte stores for fp32, 8 for
-// bf16, 4 for fp8).  MLA: one workgroup per request copies its 1152-byte
-// latent with 16-byte stores.
+// bf16, 4 for fp8 K; fp8 V blocks are tiled, fp8_v_byte in da_common.h, so
+// the four codes of an fp8 V row go to their own bytes).  MLA: one workgroup
+// per request copies its 1152-byte latent with 16-byte stores.
 #include <hip/hip_ext.h>
 
 #include "da_common.h"
@@ -56,7 +57,7 @@ __device__ __forceinline__ typename Quad<IN>::T load_quad(const void* src, int64
 }
 
 template <int IN, int OUT>
-__device__ __forceinline__ void store_quad(const AppendArgs& a, int which, int j, int64_t di,
+__device__ __forceinline__ void store_quad(const AppendArgs& a, int which, int j, int r, int d, int64_t di,
                                            typename Quad<IN>::T w) {
     if constexpr (IN == kF32 && OUT == kF32) {
         *reinterpret_cast<float4*>(static_cast<float*>(a.kv) + di) = w;
@@ -69,7 +70,17 @@ __device__ __forceinline__ void store_quad(const AppendArgs& a, int which, int j
         const uint32_t c1 = f32_to_e4m3(bf16_hi(w.x) / s);
         const uint32_t c2 = f32_to_e4m3(bf16_lo(w.y) / s);
         const uint32_t c3 = f32_to_e4m3(bf16_hi(w.y) / s);
-        *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.kv) + di) = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+        uint8_t* kv = static_cast<uint8_t*>(a.kv);
+        if (which == 0) {
+            *reinterpret_cast<uint32_t*>(kv + di) = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+        } else {
+            // the V block of (page, head) starts at di - r D - d
+            uint8_t* block = kv + (di - static_cast<int64_t>(r) * a.head_dim - d);
+            block[fp8_v_byte(r, d, a.head_dim)] = static_cast<uint8_t>(c0);
+            block[fp8_v_byte(r, d + 1, a.head_dim)] = static_cast<uint8_t>(c1);
+            block[fp8_v_byte(r, d + 2, a.head_dim)] = static_cast<uint8_t>(c2);
+            block[fp8_v_byte(r, d + 3, a.head_dim)] = static_cast<uint8_t>(c3);
+        }
     }
 }
 
@@ -89,7 +100,7 @@ __global__ __launch_bounds__(kAppendBlock) void kv_append_kernel(AppendArgs a) {
         const int j = e / D;
         const int d = e % D;
         const int64_t di = (((static_cast<int64_t>(pg) * 2 + which) * a.kv_heads + j) * a.page_size + r) * D + d;
-        store_quad<IN, OUT>(a, which, j, di, load_quad<IN>(src, s0 + e));
+        store_quad<IN, OUT>(a, which, j, r, d, di, load_quad<IN>(src, s0 + e));
     }
 }
 

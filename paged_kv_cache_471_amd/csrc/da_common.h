@@ -96,6 +96,20 @@ __device__ __forceinline__ int sload_i32(const int32_t* p) {
     return v;
 }
 
+// Byte of (slot, dim d) within the V block [P][D] of one (page, KV head) of
+// an fp8 cache: the block is kept in 16-token tiles (16 D bytes each), and
+// within a tile, with DL = D / 16 (D = 64 or 128), the code of token s and dim
+// d sits at 1024 ((d mod DL) / 4) + 256 (s / 4) + 16 (d / DL) + 4 (d mod 4) +
+// (s mod 4): lane (R, C) of a wavefront reading 16-byte pieces at 1024 p +
+// 16 (16 R + C) receives, for tokens 4R..4R+3, the codes of dims C DL + 4p ..
+// C DL + 4p + 3, one dim per 32-bit word.
+__device__ __forceinline__ int fp8_v_byte(int slot, int d, int head_dim) {
+    const int DL = head_dim >> 4;
+    const int s = slot & 15;
+    return (slot >> 4) * 16 * head_dim + 1024 * ((d & (DL - 1)) >> 2) + 256 * (s >> 2) + 16 * (d / DL) +
+           4 * (d & 3) + (s & 3);
+}
+
 // Address function of the paged GQA cache [num_pages][2][Hkv][P][D]:
 // element offset of (page, sel = 0 key / 1 value, kv head, slot, dim 0).
 __device__ __forceinline__ int64_t gqa_kv_offset(int page, int sel, int head, int slot, int num_kv_heads,

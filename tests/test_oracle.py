@@ -26,8 +26,13 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 # ----------------------------------------------------------------------------- helpers
 
-def _tiny_case(B=3, Hq=4, Hkv=2, D=8, P=4, lens=(1, 5, 9), seed=7, kv_dtype=wl.F32, q_dtype=wl.F32,
+def _tiny_case(B=3, Hq=4, Hkv=2, D=None, P=None, lens=(1, 5, 9), seed=7, kv_dtype=wl.F32, q_dtype=wl.F32,
                poison=True, extra=2):
+    # an fp8 cache's tiled V blocks need head_dim a multiple of 64 and pages of 16k tokens
+    if D is None:
+        D = 64 if kv_dtype == wl.FP8 else 8
+    if P is None:
+        P = 16 if kv_dtype == wl.FP8 else 4
     cfg = wl.GQAConfig("t", 0, B, Hq, Hkv, D, P, q_dtype, kv_dtype, "uniform:1:16")
     return wl.make_gqa_case(cfg, seq_lens=np.array(lens, dtype=np.int32), seed=seed,
                             poison=poison, extra_pages=extra, scale=0.37)
@@ -46,6 +51,9 @@ def _brute_force(case):
     qf = ofmt.decode_storage(case.q, cfg.q_dtype)
     B, Hq, D = qf.shape
     g = Hq // cfg.kv_heads
+    # an fp8 cache keeps V in tiles; read it back in token order with the
+    # input generator's inverse of its storage map
+    vlog = wl.fp8_v_from_storage(case.kv[:, 1]) if cfg.kv_dtype == wl.FP8 else case.kv[:, 1]
     out = np.zeros((B, Hq, D))
     lse = np.zeros((B, Hq))
     for b in range(B):
@@ -60,7 +68,7 @@ def _brute_force(case):
                 page = int(case.page_table[b][t // cfg.page_size])
                 slot = t % cfg.page_size
                 k = ofmt.decode_storage(case.kv[page, 0, j, slot], cfg.kv_dtype)
-                v = ofmt.decode_storage(case.kv[page, 1, j, slot], cfg.kv_dtype)
+                v = ofmt.decode_storage(vlog[page, j, slot], cfg.kv_dtype)
                 if cfg.kv_dtype == wl.FP8:
                     k = k * float(case.k_scale[j])
                     v = v * float(case.v_scale[j])
@@ -242,10 +250,12 @@ def test_fp8_scales_apply_per_kv_head():
     case.v_scale = np.array([2.0, 0.25], dtype=np.float32)
     out0, lse0 = _run(case)
     table = ofmt.fp8_e4m3fn_table()
-    kv32 = table[case.kv].astype(np.float32)
+    logical = case.kv.copy()
+    logical[:, 1] = wl.fp8_v_from_storage(case.kv[:, 1])        # V in token order
+    kv32 = table[logical].astype(np.float32)
     kv32[:, 0] *= case.k_scale[None, :, None, None]
     kv32[:, 1] *= case.v_scale[None, :, None, None]
-    f32cfg = wl.GQAConfig("f", 0, 3, 4, 2, 8, 4, wl.F32, wl.F32, "uniform:1:16")
+    f32cfg = wl.GQAConfig("f", 0, 3, 4, 2, case.cfg.head_dim, case.cfg.page_size, wl.F32, wl.F32, "uniform:1:16")
     ref = wl.GQACase(f32cfg, case.seq_lens, case.page_table, case.num_pages, case.q, kv32, None, None,
                      case.scale, case.unreferenced)
     out1, lse1 = _run(ref)

@@ -37,7 +37,7 @@ def _case(rng, B, n, Hq, Hkv, D, lens, kv_dtype=F32, P=16):
     else:
         kc, ks = wl.quantize_fp8_per_head(kv32[:, 0], head_axis=1)
         vc, vs = wl.quantize_fp8_per_head(kv32[:, 1], head_axis=1)
-        kv = np.stack([kc, vc], axis=1)
+        kv = np.stack([kc, wl.fp8_v_to_storage(vc)], axis=1)     # V blocks in the tiled fp8 format
     q = q32 if q_dtype == F32 else wl.to_bf16_bits(q32)
     return dict(q=q, q_dtype=q_dtype, kv=kv, kv_dtype=kv_dtype, table=table, lens=lens, P=P, ks=ks, vs=vs)
 
@@ -49,10 +49,11 @@ def _dense_history(c, b):
     Hkv, D = c["kv"].shape[2], c["kv"].shape[4]
     K = np.zeros((L, Hkv, D))
     V = np.zeros((L, Hkv, D))
+    vlog = wl.fp8_v_from_storage(c["kv"][:, 1]) if c["kv_dtype"] == FP8 else c["kv"][:, 1]
     for t in range(L):
         pg = c["table"][b, t // P]
         K[t] = dec(c["kv"][pg, 0, :, t % P, :], c["kv_dtype"])
-        V[t] = dec(c["kv"][pg, 1, :, t % P, :], c["kv_dtype"])
+        V[t] = dec(vlog[pg, :, t % P, :], c["kv_dtype"])
     if c["kv_dtype"] == FP8:
         K *= c["ks"].astype(np.float64)[None, :, None]
         V *= c["vs"].astype(np.float64)[None, :, None]
@@ -98,7 +99,7 @@ def test_every_token_a_row_equals_torch_causal_sdpa(kv_dtype, Hq, Hkv):
     torch's scaled_dot_product_attention(is_causal=True) computes."""
     rng = np.random.default_rng(11 + Hq + Hkv + kv_dtype)
     n = 21
-    c = _case(rng, 2, n, Hq, Hkv, 32, [n, n], kv_dtype)
+    c = _case(rng, 2, n, Hq, Hkv, 64 if kv_dtype == FP8 else 32, [n, n], kv_dtype)
     scale = 0.3
     out, lse = _run(c, scale)
     qf = oracle.decode_storage(c["q"], c["q_dtype"])

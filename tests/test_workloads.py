@@ -37,7 +37,7 @@ def test_page_table_is_a_permutation():
 
 
 def test_fp8_quantiser_uses_full_range_per_head():
-    cfg = wl.GQAConfig("f", 5, 2, 4, 2, 16, 16, wl.BF16, wl.FP8, "fixed:40")
+    cfg = wl.GQAConfig("f", 5, 2, 4, 2, 64, 16, wl.BF16, wl.FP8, "fixed:40")
     c = wl.make_gqa_case(cfg)
     from oracle.formats import fp8_e4m3fn_to_f64
     for kv_i, sc in ((0, c.k_scale), (1, c.v_scale)):
@@ -45,6 +45,20 @@ def test_fp8_quantiser_uses_full_range_per_head():
             v = fp8_e4m3fn_to_f64(c.kv[:, kv_i, j])
             assert np.nanmax(np.abs(v)) == 448.0
             assert sc[j] > 0
+
+
+def test_fp8_poison_lands_outside_history_in_the_tiled_v_format():
+    """With an fp8 cache the V blocks are stored tiled; read back in token
+    order, every history token is finite and every slot past it is the NaN code."""
+    cfg = wl.GQAConfig("p", 6, 3, 8, 2, 128, 16, wl.BF16, wl.FP8, "uniform:1:60")
+    c = wl.make_gqa_case(cfg, poison=True, extra_pages=1)
+    v = wl.fp8_v_from_storage(c.kv[:, 1])
+    for b, L in enumerate(c.seq_lens):
+        for t in range(int(L)):
+            assert np.all(v[c.page_table[b, t // 16], :, t % 16] != wl.FP8_POISON)
+        r = int(L) % 16
+        if r:
+            assert np.all(v[c.page_table[b, (int(L) - 1) // 16], :, r:] == wl.FP8_POISON)
 
 
 def test_poison_only_outside_history():

@@ -213,6 +213,41 @@ def _normal(rng, shape, std, dtype=np.float32):
     return x
 
 
+def fp8_v_tile_index(page_size: int, head_dim: int) -> np.ndarray:
+    """Storage format of an fp8 cache's V blocks: the [P][D] block of one
+    (page, KV head) is kept in 16-token tiles, and within a tile the code of
+    token t and dim d (with DL = D / 16) sits at byte
+        1024 * ((d % DL) // 4) + 16 * (16 * ((t % 16) // 4) + d // DL) + 4 * (d % 4) + t % 4,
+    i.e. for each group of four tokens and each dim their four codes are
+    adjacent.  Returns the storage byte of every (t, d), shape [P][D]."""
+    P, D = page_size, head_dim
+    if D % 64 != 0 or P % 16 != 0:
+        raise ValueError("the tiled fp8 V format needs head_dim a multiple of 64 and pages of 16k tokens")
+    DL = D // 16
+    t = np.arange(P)[:, None]
+    d = np.arange(D)[None, :]
+    return ((t // 16) * 16 * D + 1024 * ((d % DL) // 4) + 16 * (16 * ((t % 16) // 4) + d // DL)
+            + 4 * (d % 4) + t % 4).astype(np.int64)
+
+
+def fp8_v_to_storage(v: np.ndarray) -> np.ndarray:
+    """Logical fp8 V codes [..][P][D] -> the tiled storage of the same shape."""
+    P, D = v.shape[-2:]
+    idx = fp8_v_tile_index(P, D).reshape(-1)
+    flat = v.reshape(v.shape[:-2] + (P * D,))
+    out = np.empty_like(flat)
+    out[..., idx] = flat
+    return out.reshape(v.shape)
+
+
+def fp8_v_from_storage(v: np.ndarray) -> np.ndarray:
+    """Tiled storage of fp8 V codes [..][P][D] -> logical [..][P][D] (token-major)."""
+    P, D = v.shape[-2:]
+    idx = fp8_v_tile_index(P, D).reshape(-1)
+    flat = v.reshape(v.shape[:-2] + (P * D,))
+    return flat[..., idx].reshape(v.shape)
+
+
 def _poison_tail_gqa(kv, seq_lens, table, page_size, kv_dtype, unreferenced):
     for b, L in enumerate(seq_lens):
         r = int(L) % page_size
@@ -260,6 +295,8 @@ def make_gqa_case(cfg: GQAConfig, *, seq_lens: Optional[np.ndarray] = None, batc
     del kv32
     if poison:
         _poison_tail_gqa(kv, seq_lens, table, cfg.page_size, cfg.kv_dtype, unref)
+    if cfg.kv_dtype == FP8:
+        kv[:, 1] = fp8_v_to_storage(kv[:, 1])
     return GQACase(cfg, seq_lens, table, num_pages, q, kv, k_scale, v_scale,
                    cfg.scale if scale is None else float(scale), unref)
 
