@@ -88,10 +88,29 @@ def gqa_kernel_name(cfg, rows: int = 1) -> str:
     """The GQA attention kernel the library runs for this head shape."""
     import workloads as wl
     members = rows * cfg.q_heads // cfg.kv_heads
-    mfma = cfg.q_dtype == wl.BF16 and 4 <= members <= 16
-    if os.environ.get("DA_GQA_VECTOR") == "1" and members <= 8:
-        mfma = False
+    if cfg.kv_dtype == wl.FP8:          # fp8 V tiles are read by the matrix-core kernel only
+        mfma = cfg.q_dtype == wl.BF16 and members <= 16
+    else:
+        mfma = cfg.q_dtype == wl.BF16 and 4 <= members <= 16
+        if os.environ.get("DA_GQA_VECTOR") == "1" and members <= 8:
+            mfma = False
     return "gqa_mfma_kernel" if mfma else "gqa_attn_kernel"
+
+
+def headline_kernel(cfg, rows: int, default_shape: bool):
+    """(kernel name, its source list, its committed HBM-counter summary or None)
+    for the dominant kernel of a headline workload.  The counter summaries hold
+    one workload each (llama8b; mla at 128 heads): any other headline reports
+    traffic as null rather than another workload's bytes."""
+    import workloads as wl
+    if isinstance(cfg, wl.MLAConfig):
+        if cfg.q_heads == 128:
+            pmc = MLA_PMC_FILE if (cfg.name == "mla" and rows == 1 and default_shape) else None
+            return "mla_wave_kernel", MLA_KERNEL_SOURCES, pmc
+        return "mla_attn_kernel", None, None
+    name = gqa_kernel_name(cfg, rows)
+    pmc = PMC_FILE if (cfg.name == "llama8b" and rows == 1 and default_shape and name == "gqa_mfma_kernel") else None
+    return name, KERNEL_SOURCES if name == "gqa_mfma_kernel" else None, pmc
 
 
 def workload_desc(cfg) -> str:
@@ -726,7 +745,9 @@ def main():
     appends = {cfg.name: time_append(runner, args.steps, args.warmup, ms)}
     gbs = runner.bytes / (ms * 1e-3) / 1e9
     kern_gbs = runner.bytes / (kms * 1e-3) / 1e9 if kms else None
-    traffic = traffic_from_profiles()
+    rows_h = ROWS_WORKLOADS[args.workload][1] if args.workload in ROWS_WORKLOADS else 1
+    kname, ksrc, kpmc = headline_kernel(cfg, rows_h, not (args.heads or args.kv_heads))
+    traffic = traffic_from_profiles(kpmc, ksrc) if kpmc else None
 
     result = {
         "metric": METRIC,
@@ -748,14 +769,14 @@ def main():
         "algorithmic_bytes_per_step": runner.bytes,
         "roofline": {
             "bound": "hbm",
-            "kernel": "mla_attn_kernel" if isinstance(cfg, wl.MLAConfig) else gqa_kernel_name(cfg),
+            "kernel": kname,
             "achieved": round(kern_gbs, 2) if kern_gbs else None,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(kern_gbs / HBM_PEAK_GBS, 4) if kern_gbs else None,
             "traffic": traffic,
             "kernel_ms": kms,
-            "kernel_source_hash": kernel_hash(),
+            "kernel_source_hash": kernel_hash(ksrc) if ksrc else None,
         },
     }
 

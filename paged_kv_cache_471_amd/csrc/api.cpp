@@ -284,8 +284,7 @@ bool gqa_uses_mfma(const da_paged_desc* d, int q_rows) {
     // kernel reads: every group size runs there
     if (d->kv_dtype == DA_FP8_E4M3) return d->q_dtype == DA_BF16 && want <= 16;
     if (want <= 8 && vector_forced()) return false;
-    return d->q_dtype == DA_BF16 && (d->kv_dtype == DA_BF16 || d->kv_dtype == DA_FP8_E4M3) && want >= 4 &&
-           want <= 16;
+    return d->q_dtype == DA_BF16 && d->kv_dtype == DA_BF16 && want >= 4 && want <= 16;
 }
 
 // (row, head) members of one KV head's group in the GQA kernels: q_rows times

@@ -75,3 +75,23 @@ def test_mla_counters_reported_only_for_the_profiled_kernel_source(monkeypatch):
     monkeypatch.setattr(bench, "kernel_hash", lambda sources=None: "0" * 16)
     assert bench.counters_from_profiles(sq, bench.MLA_KERNEL_SOURCES) is None
     assert bench.traffic_from_profiles(bench.MLA_PMC_FILE, bench.MLA_KERNEL_SOURCES) is None
+
+
+def test_headline_kernel_names_each_workloads_own_kernel():
+    """The headline roofline names the kernel the library runs for the chosen
+    workload and reads HBM counters only from the summary of that workload."""
+    import dataclasses
+    import workloads as wl
+    bench = _bench_module()
+    c = wl.CONFIGS
+    assert bench.headline_kernel(c["llama8b"], 1, True) == ("gqa_mfma_kernel", bench.KERNEL_SOURCES, bench.PMC_FILE)
+    # another GQA workload on the same kernel: no borrowed counters
+    assert bench.headline_kernel(c["skewed"], 1, True) == ("gqa_mfma_kernel", bench.KERNEL_SOURCES, None)
+    assert bench.headline_kernel(c["llama8b"], 2, True)[2] is None
+    assert bench.headline_kernel(c["llama8b"], 1, False)[2] is None
+    # fp8 caches run on the matrix-core kernel at every group size
+    fp8_small_group = dataclasses.replace(c["longfp8"], q_heads=2 * c["longfp8"].kv_heads)
+    assert bench.headline_kernel(fp8_small_group, 1, True)[0] == "gqa_mfma_kernel"
+    assert bench.headline_kernel(c["mla"], 1, True) == ("mla_wave_kernel", bench.MLA_KERNEL_SOURCES, bench.MLA_PMC_FILE)
+    assert bench.headline_kernel(dataclasses.replace(c["mla"], q_heads=16), 1, False) == ("mla_attn_kernel", None, None)
+    assert bench.headline_kernel(c["tiny"], 1, True)[2] is None
