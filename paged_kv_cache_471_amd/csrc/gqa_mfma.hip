@@ -174,15 +174,19 @@ __device__ __forceinline__ int k_dim(int s, int R) {
     else return 64 * (s >> 1) + 16 * R + 8 * (s & 1);
 }
 
-// Occupancy: fp8 is bounded to three workgroups (three waves per SIMD, at
-// most 168 registers each): its pages are small and the stream is bound by
-// latency (106.6 against 128.5 us on the long-context workload).  bf16 keeps
-// the compiler's own allocation (about 200 registers plus 32 accumulation
-// registers, two waves per SIMD); a tighter bound that allows three made it
-// 4-5 % slower.
+// Occupancy: fp8 is compiled for three workgroups per CU (three waves per
+// SIMD, at most 168 registers each; the compiler's own allocation, one
+// workgroup, made the long-context workload 128.5 against 106.6 us) but runs
+// two per CU by default: with 16-byte value loads two waves per SIMD keep the
+// stream busy, and a third only adds pieces to the merge (long-context
+// workload 96.0-96.8 against 102.7-103.2 us per step; every fp8 shape
+// measured was equal or faster).  bf16 keeps the compiler's own allocation
+// (about 200 registers plus 32 accumulation registers, two waves per SIMD); a
+// tighter bound that allows three made it 4-5 % slower.
 template <int KV>
 struct MOcc {
     static constexpr int blocks_per_cu = KV == kFP8 ? 3 : 1;
+    static constexpr int run_per_cu = KV == kFP8 ? 2 : 0;    // 0: as many as fit
 };
 
 // RG = log2(query heads per KV head).  Members m < 16 of a KV head's group are
@@ -549,6 +553,7 @@ hipError_t launch_m(const GqaArgs& a, hipStream_t s, const KernelEvents& ev, int
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, gqa_mfma_kernel<KV, D, RG>, kGqaBlock, 0) !=
             hipSuccess)
             return hipErrorInvalidValue;
+        if (MOcc<KV>::run_per_cu > 0 && blocks > MOcc<KV>::run_per_cu) blocks = MOcc<KV>::run_per_cu;
         *per_cu = blocks * (kGqaBlock / 64);
         return hipSuccess;
     }
