@@ -108,7 +108,9 @@ extern "C" {
  * aligned on the matrix-core path.
  *
  * workers: number of workers, 0 selects the library default (one per resident
- * wavefront).  A worker is one wavefront that processes one contiguous share
+ * wavefront; for fp8 caches two workgroups of four wavefronts per CU, fewer
+ * than fit, which measured faster).  A worker is one wavefront that
+ * processes one contiguous share
  * of all (request, KV head, page) units; see decode_attn_plan for the rule.
  * Limits: batch <= 8192, workers <= 16384.
  */
