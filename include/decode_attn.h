@@ -49,6 +49,10 @@
  *    device.  Calls on one stream are ordered; calls on different streams
  *    use different workspaces.  The _ws entry points take a workspace the
  *    caller owns instead and allocate nothing.
+ *  - Once a stream's workspace is large enough (after one call of that size
+ *    on it), a call only enqueues kernel launches on the stream: it can be
+ *    captured into a HIP graph and replayed (the graph keeps the workspace's
+ *    address, so no larger call may run on that stream meanwhile).
  */
 #ifndef DECODE_ATTN_H
 #define DECODE_ATTN_H
