@@ -99,8 +99,9 @@ extern "C" {
  *
  * Offered: head_dim in {64, 128}; page_size 16, 32, 64, 128 or 256 (the
  * kernels walk 16-token tiles of a page); num_q_heads / num_kv_heads in
- * {1, 2, 4, 8}; (q_dtype, kv_dtype) in {(F32, F32), (BF16, BF16),
- * (BF16, FP8_E4M3)}.  For fp8, k_scale and v_scale are device fp32
+ * {1, 2, 4, 8, 16} (16 with bf16 queries and one query row: at most 16
+ * (row, head) pairs per KV head on the matrix cores, 8 on the vector ALUs);
+ * (q_dtype, kv_dtype) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)}.  For fp8, k_scale and v_scale are device fp32
  * [num_kv_heads]; a stored code x of KV head j means e4m3(x) * scale[j].
  *
  * Kernels: bf16 queries with 4 to 16 query heads (or, with several query

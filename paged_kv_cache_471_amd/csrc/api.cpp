@@ -250,7 +250,7 @@ int check_paged(const da_paged_desc* d) {
     // pages of 16 << k tokens: the kernels walk 16-token tiles
     if (d->page_size < 16 || d->page_size > 256 || (d->page_size & (d->page_size - 1)) != 0)
         return DA_ERR_UNSUPPORTED;
-    if (group != 1 && group != 2 && group != 4 && group != 8) return DA_ERR_UNSUPPORTED;
+    if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16) return DA_ERR_UNSUPPORTED;
     if (d->batch > da::kMaxBatch || d->workers > da::kMaxWorkers) return DA_ERR_UNSUPPORTED;
     const int64_t units_bound =
         static_cast<int64_t>(d->num_kv_heads) * d->batch * d->max_pages_per_seq * (d->page_size / 16);

@@ -576,6 +576,7 @@ hipError_t by_rg(int rg, const GqaArgs* a, hipStream_t s, const KernelEvents& ev
         case 1: return launch_m<KV, D, 1>(args, s, ev, per_cu);
         case 2: return launch_m<KV, D, 2>(args, s, ev, per_cu);
         case 3: return launch_m<KV, D, 3>(args, s, ev, per_cu);
+        case 4: return launch_m<KV, D, 4>(args, s, ev, per_cu);
         default: return hipErrorInvalidValue;
     }
 }

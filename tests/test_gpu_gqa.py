@@ -60,6 +60,20 @@ def test_dtypes_groups_dims(qd, kd, Hq, Hkv, D):
     assert_close_gqa(case, out, lse, ro, rl, label=f"{qd}/{kd} {Hq}/{Hkv} D{D}")
 
 
+@pytest.mark.parametrize("kd", [wl.BF16, wl.FP8])
+@pytest.mark.parametrize("Hq,Hkv,D,P,workers", [(128, 8, 128, 16, 0), (32, 2, 64, 64, 0), (128, 8, 128, 32, 777)])
+def test_group_of_sixteen(kd, Hq, Hkv, D, P, workers):
+    """16 query heads per KV head (a full 16-member tile of the matrix-core
+    kernel; the 128/8 head shape of the largest Llama-3 models)."""
+    cfg = wl.GQAConfig("g16", 9, 7, Hq, Hkv, D, P, wl.BF16, kd, "lognormal:600:1.0:1:5000")
+    case = wl.make_gqa_case(cfg, poison=True, extra_pages=2, seed=160 + D + P + kd)
+    case.seq_lens[2] = 0
+    case.seq_lens[4] = 1
+    out, lse, _ = run(case, workers=workers)
+    ro, rl = gqa_oracle(case)
+    assert_close_gqa(case, out, lse, ro, rl, label=f"group 16 {Hq}/{Hkv} D{D} P{P} kv{kd}")
+
+
 # ----------------------------------------------------------------------------- edge lengths and partitions
 
 @pytest.mark.parametrize("lens", [[1], [15], [16], [17], [31, 32, 33], [1, 0, 2], [0], [0, 0, 5],
