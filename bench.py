@@ -90,6 +90,8 @@ def gqa_kernel_name(cfg, rows: int = 1) -> str:
     members = rows * cfg.q_heads // cfg.kv_heads
     if cfg.kv_dtype == wl.FP8:          # fp8 V tiles are read by the matrix-core kernel only
         mfma = cfg.q_dtype == wl.BF16 and members <= 16
+    elif (cfg.q_heads // cfg.kv_heads) & (cfg.q_heads // cfg.kv_heads - 1):   # group not a power of two
+        mfma = cfg.q_dtype == wl.BF16 and members <= 16
     else:
         mfma = cfg.q_dtype == wl.BF16 and 4 <= members <= 16
         if os.environ.get("DA_GQA_VECTOR") == "1" and members <= 8:

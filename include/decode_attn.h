@@ -98,17 +98,19 @@ extern "C" {
  * seq_lens: int32 [batch].
  *
  * Offered: head_dim in {64, 128}; page_size 16, 32, 64, 128 or 256 (the
- * kernels walk 16-token tiles of a page); num_q_heads / num_kv_heads in
- * {1, 2, 4, 8, 16} (16 with bf16 queries and one query row: at most 16
- * (row, head) pairs per KV head on the matrix cores, 8 on the vector ALUs);
- * (q_dtype, kv_dtype) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)}.  For fp8, k_scale and v_scale are device fp32
+ * kernels walk 16-token tiles of a page); num_q_heads / num_kv_heads from
+ * 1 to 16, with at most 16 (row, head) pairs per KV head on the matrix cores
+ * and 8 on the vector ALUs; group sizes that are not a power of two, and
+ * groups of 16, need bf16 queries (matrix cores); (q_dtype, kv_dtype) in
+ * {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)}.  For fp8, k_scale and v_scale are device fp32
  * [num_kv_heads]; a stored code x of KV head j means e4m3(x) * scale[j].
  *
  * Kernels: bf16 queries with 4 to 16 query heads (or, with several query
  * rows, row x head pairs) per KV head run on the matrix cores (scores and
  * values as MFMA products, softmax weights kept in fp32, split into two bf16
  * terms for the fp8 value product); fp8 caches run there for every group
- * size; fp32 queries and bf16 groups of 1 or 2 on the vector ALUs.  Both
+ * size, and so do groups that are not a power of two; fp32 queries and
+ * bf16 groups of 1 or 2 on the vector ALUs.  Both
  * give the same semantics and the same tolerances; kv_pages must be 16-byte
  * aligned on the matrix-core path.
  *

@@ -250,7 +250,10 @@ int check_paged(const da_paged_desc* d) {
     // pages of 16 << k tokens: the kernels walk 16-token tiles
     if (d->page_size < 16 || d->page_size > 256 || (d->page_size & (d->page_size - 1)) != 0)
         return DA_ERR_UNSUPPORTED;
-    if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16) return DA_ERR_UNSUPPORTED;
+    // any group up to 16 query heads per KV head; groups that are not a power
+    // of two run on the matrix-core kernel only, so they need bf16 queries
+    if (group > 16) return DA_ERR_UNSUPPORTED;
+    if ((group & (group - 1)) != 0 && d->q_dtype != DA_BF16) return DA_ERR_UNSUPPORTED;
     if (d->batch > da::kMaxBatch || d->workers > da::kMaxWorkers) return DA_ERR_UNSUPPORTED;
     const int64_t units_bound =
         static_cast<int64_t>(d->num_kv_heads) * d->batch * d->max_pages_per_seq * (d->page_size / 16);
@@ -283,6 +286,9 @@ bool gqa_uses_mfma(const da_paged_desc* d, int q_rows) {
     // fp8 caches keep their V blocks in tiles that only the matrix-core
     // kernel reads: every group size runs there
     if (d->kv_dtype == DA_FP8_E4M3) return d->q_dtype == DA_BF16 && want <= 16;
+    // the vector kernel maps members to heads with shifts: powers of two only
+    const int group = d->num_q_heads / d->num_kv_heads;
+    if ((group & (group - 1)) != 0) return d->q_dtype == DA_BF16 && want <= 16;
     if (want <= 8 && vector_forced()) return false;
     return d->q_dtype == DA_BF16 && d->kv_dtype == DA_BF16 && want >= 4 && want <= 16;
 }
@@ -306,7 +312,7 @@ int resolve_gqa_workers(const da_paged_desc* d, int members, bool mfma, int* G) 
     int st = device_cus(&cus);
     if (st != DA_OK) return st;
     const int group_log2 = __builtin_ctz(static_cast<unsigned>(d->num_q_heads / d->num_kv_heads));
-    const int per_cu = mfma ? da::gqa_mfma_workers_per_cu(d->kv_dtype, d->head_dim, group_log2)
+    const int per_cu = mfma ? da::gqa_mfma_workers_per_cu(d->kv_dtype, d->head_dim)
                             : da::gqa_workers_per_cu(d->q_dtype, d->kv_dtype, d->head_dim, members, group_log2);
     if (per_cu <= 0) return DA_ERR_UNSUPPORTED;
     int g = cus * per_cu;
@@ -454,7 +460,7 @@ int gqa_step(const da_paged_desc* d, int q_rows, const void* q, const void* kv_p
     ma.group = members;
     ma.dim = d->head_dim;
     ma.rows = q_rows;
-    ma.group_log2 = group_log2;
+    ma.heads_per_unit = group;
     // Streams split into about two pieces or fewer are merged by one
     // workgroup for all the heads of their group (fewer, fuller workgroups;
     // most of them return at once); more deeply split streams by one
@@ -570,7 +576,7 @@ int mla_step(const da_mla_desc* dd, int q_rows, const void* q, const void* kv_pa
     mg.group = d->num_heads;
     mg.dim = d->v_dim;
     mg.rows = 1;
-    mg.group_log2 = __builtin_ctz(static_cast<unsigned>(d->num_heads));
+    mg.heads_per_unit = d->num_heads;
     // four heads per merge workgroup: two float4 columns of [4][512] per
     // thread, both loaded in one pass (measured: 20.4 us against 20.8 with
     // eight heads and four columns per thread)

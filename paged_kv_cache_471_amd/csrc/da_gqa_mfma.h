@@ -6,10 +6,11 @@
 namespace da {
 
 // q bf16, K/V bf16 or fp8, head_dim 64 or 128; up to 16 (row, head) members
-// per KV head (a.q_rows rows of 2^a.group_log2 heads).  The partial slots hold
-// the members padded to a power of two, as the merge kernel reads them.
+// per KV head (a.q_rows rows of q_heads / kv_heads heads, any count).  The
+// partial slots hold the members padded to a power of two, as the merge
+// kernel reads them.
 hipError_t launch_gqa_mfma(int kv_dtype, int head_dim, const GqaArgs& a, hipStream_t s, const KernelEvents& ev);
-// Workers (one wavefront each) of that kernel that fit on one CU at once (0 if none).
-int gqa_mfma_workers_per_cu(int kv_dtype, int head_dim, int group_log2);
+// Workers (one wavefront each) of that kernel that run on one CU by default (0 if none).
+int gqa_mfma_workers_per_cu(int kv_dtype, int head_dim);
 
 }  // namespace da

@@ -40,7 +40,8 @@ struct GqaArgs {
     // sees history positions t <= len - q_rows + i.  The kernel's head group
     // GS holds the q_rows x (q_heads / kv_heads) (row, head) pairs of one KV
     // head, row-major, padded to a power of two; group_log2 = log2 of the
-    // query heads per KV head.
+    // query heads per KV head, read by the vector kernel only (powers of two);
+    // the matrix-core kernel takes any count q_heads / kv_heads.
     int q_rows, group_log2;
     int2* plan_info;        // [1]: (W, active workers), written by worker 0
     int2* stream_info;      // [batch * kv_heads]: (first unit, pieces) of each non-empty stream
@@ -90,16 +91,16 @@ struct MergeArgs {
     const int2* stream_info;
     const float* o_part;    // [2 * workers][group][dim]
     const float* lse_part;  // [2 * workers][group]  (log2 domain)
-    void* out;              // [batch][rows][units << group_log2][dim], bf16 or fp32
-    float* lse;             // [batch][rows][units << group_log2] or null
+    void* out;              // [batch][rows][units * heads_per_unit][dim], bf16 or fp32
+    float* lse;             // [batch][rows][units * heads_per_unit] or null
     int units;              // streams per request (KV heads, or 1 for MLA)
     int group;              // (row, head) slots per stream in the partials
     int dim;                // values per head
     int heads_per_block;    // divides group
     int col_chunks;         // power of two dividing heads_per_block * dim / 4 (1: whole heads)
     int out_is_bf16;
-    int rows;               // query rows per request; slot h is row h >> group_log2
-    int group_log2;         // log2 of the query heads per stream
+    int rows;               // query rows per request; slot h is row h / heads_per_unit
+    int heads_per_unit;     // query heads per stream (any count)
 };
 
 struct GatherArgs {

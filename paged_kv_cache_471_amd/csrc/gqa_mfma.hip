@@ -189,13 +189,13 @@ struct MOcc {
     static constexpr int run_per_cu = KV == kFP8 ? 2 : 0;    // 0: as many as fit
 };
 
-// RG = log2(query heads per KV head).  Members m < 16 of a KV head's group are
-// (row m >> RG, head m & (2^RG - 1)); a.q_rows rows.
-template <int KV, int D, int RG>
+// With gs = q_heads / kv_heads query heads per KV head (any count up to 16),
+// member m < 16 of a KV head's group is (row m / gs, head m % gs); a.q_rows
+// rows; members from q_rows * gs up only pad the tile.
+template <int KV, int D>
 __global__ __launch_bounds__(kGqaBlock, MOcc<KV>::blocks_per_cu) void gqa_mfma_kernel(GqaArgs a) {
     using C = MCfg<KV, D>;
     constexpr int KS = C::KS, KW = C::KW, DL = C::DL, VW = C::VW, EB = C::EB, NB = C::NB;
-    constexpr int G = 1 << RG;
 
     const int lane = threadIdx.x & 63;
     const int R = lane >> 4;
@@ -205,8 +205,9 @@ __global__ __launch_bounds__(kGqaBlock, MOcc<KV>::blocks_per_cu) void gqa_mfma_k
     const int Hkv = a.kv_heads;
     const int Hq = a.q_heads;
     const int NR = a.q_rows;
+    const int gs = Hq / Hkv;                      // query heads per KV head
     int MT = 1;                                   // members per stream in the partial slots
-    while (MT < (NR << RG)) MT <<= 1;
+    while (MT < NR * gs) MT <<= 1;
 
     const WaveShare sh = plan_share(a.seq_lens, a.batch, kPage, Hkv, a.workers, g);
     if (sh.has_empty) {
@@ -228,7 +229,8 @@ __global__ __launch_bounds__(kGqaBlock, MOcc<KV>::blocks_per_cu) void gqa_mfma_k
     const int tile_mask = (1 << a.tile_shift) - 1;
 
     // member of this lane's score column, and its row / query head offset
-    const int mrow = Cc >> RG;                       // query row of member Cc
+    const int mrow = Cc / gs;                        // query row of member Cc
+    const int mhead = Cc - mrow * gs;                // its query head within the KV head's group
     const bool mlive = mrow < NR;                    // real member (not padding)
 
     Cursor cc;
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(kGqaBlock, MOcc<KV>::blocks_per_cu) void gqa_mfma_k
     // Q^T operand: member Cc, the 8 dims k_dim(s, R) of every step
     bf16x8_t qop[KS];
     auto load_q = [&](int b, int j) {
-        const int64_t row = (static_cast<int64_t>(b) * NR + mrow) * Hq + (j << RG) + (Cc & (G - 1));
+        const int64_t row = (static_cast<int64_t>(b) * NR + mrow) * Hq + j * gs + mhead;
         const uint16_t* src = static_cast<const uint16_t*>(a.q) + row * D;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -427,7 +429,7 @@ __global__ __launch_bounds__(kGqaBlock, MOcc<KV>::blocks_per_cu) void gqa_mfma_k
             if (mlive) {
                 const int d0 = 4 * R * DL;
                 if (whole) {
-                    const int64_t row = (static_cast<int64_t>(cc.b) * NR + mrow) * Hq + (cc.j << RG) + (Cc & (G - 1));
+                    const int64_t row = (static_cast<int64_t>(cc.b) * NR + mrow) * Hq + cc.j * gs + mhead;
                     uint16_t* dst = static_cast<uint16_t*>(a.out) + row * D + d0;
                     uint32_t packed[2 * DL];
 #pragma unroll
@@ -453,9 +455,11 @@ __global__ __launch_bounds__(kGqaBlock, MOcc<KV>::blocks_per_cu) void gqa_mfma_k
         for (int x = 0; x < (KV == kFP8 ? 0 : 4); ++x) {
             const int mem = 4 * R + x;
             const float inv = __shfl(inv_col, mem, 64);
-            if ((mem >> RG) >= NR) continue;
+            const int mem_row = mem / gs;
+            if (mem_row >= NR) continue;
             if (whole) {
-                const int64_t row = (static_cast<int64_t>(cc.b) * NR + (mem >> RG)) * Hq + (cc.j << RG) + (mem & (G - 1));
+                const int64_t row =
+                    (static_cast<int64_t>(cc.b) * NR + mem_row) * Hq + cc.j * gs + (mem - mem_row * gs);
                 uint16_t* dst = static_cast<uint16_t*>(a.out) + row * D + Cc * DL;
                 uint32_t packed[DL / 2];
 #pragma unroll
@@ -473,7 +477,7 @@ __global__ __launch_bounds__(kGqaBlock, MOcc<KV>::blocks_per_cu) void gqa_mfma_k
         if (R == 0 && mlive) {
             if (whole) {
                 if (a.lse != nullptr) {
-                    const int64_t row = (static_cast<int64_t>(cc.b) * NR + mrow) * Hq + (cc.j << RG) + (Cc & (G - 1));
+                    const int64_t row = (static_cast<int64_t>(cc.b) * NR + mrow) * Hq + cc.j * gs + mhead;
                     a.lse[row] = lse2 * kLn2;
                 }
             } else {
@@ -546,59 +550,42 @@ __global__ __launch_bounds__(kGqaBlock, MOcc<KV>::blocks_per_cu) void gqa_mfma_k
     }
 }
 
-template <int KV, int D, int RG>
-hipError_t launch_m(const GqaArgs& a, hipStream_t s, const KernelEvents& ev, int* per_cu) {
+template <int KV, int D>
+hipError_t launch_m(const GqaArgs* a, hipStream_t s, const KernelEvents& ev, int* per_cu) {
     if (per_cu != nullptr) {
         int blocks = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, gqa_mfma_kernel<KV, D, RG>, kGqaBlock, 0) !=
-            hipSuccess)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, gqa_mfma_kernel<KV, D>, kGqaBlock, 0) != hipSuccess)
             return hipErrorInvalidValue;
         if (MOcc<KV>::run_per_cu > 0 && blocks > MOcc<KV>::run_per_cu) blocks = MOcc<KV>::run_per_cu;
         *per_cu = blocks * (kGqaBlock / 64);
         return hipSuccess;
     }
     const int per_block = kGqaBlock / 64;
-    const int grid = (a.workers + per_block - 1) / per_block;
+    const int grid = (a->workers + per_block - 1) / per_block;
     if (ev.start != nullptr)
-        hipExtLaunchKernelGGL((gqa_mfma_kernel<KV, D, RG>), dim3(grid), dim3(kGqaBlock), 0, s, ev.start, ev.stop,
-                              0, a);
+        hipExtLaunchKernelGGL((gqa_mfma_kernel<KV, D>), dim3(grid), dim3(kGqaBlock), 0, s, ev.start, ev.stop, 0, *a);
     else
-        hipLaunchKernelGGL((gqa_mfma_kernel<KV, D, RG>), dim3(grid), dim3(kGqaBlock), 0, s, a);
+        hipLaunchKernelGGL((gqa_mfma_kernel<KV, D>), dim3(grid), dim3(kGqaBlock), 0, s, *a);
     return hipGetLastError();
 }
 
-template <int KV, int D>
-hipError_t by_rg(int rg, const GqaArgs* a, hipStream_t s, const KernelEvents& ev, int* per_cu) {
-    const GqaArgs dummy{};
-    const GqaArgs& args = a ? *a : dummy;
-    switch (rg) {
-        case 0: return launch_m<KV, D, 0>(args, s, ev, per_cu);
-        case 1: return launch_m<KV, D, 1>(args, s, ev, per_cu);
-        case 2: return launch_m<KV, D, 2>(args, s, ev, per_cu);
-        case 3: return launch_m<KV, D, 3>(args, s, ev, per_cu);
-        case 4: return launch_m<KV, D, 4>(args, s, ev, per_cu);
-        default: return hipErrorInvalidValue;
-    }
-}
-
-hipError_t dispatch_m(int kv_dtype, int dim, int rg, const GqaArgs* a, hipStream_t s, const KernelEvents& ev,
-                      int* per_cu) {
-    if (kv_dtype == kBF16 && dim == 128) return by_rg<kBF16, 128>(rg, a, s, ev, per_cu);
-    if (kv_dtype == kBF16 && dim == 64) return by_rg<kBF16, 64>(rg, a, s, ev, per_cu);
-    if (kv_dtype == kFP8 && dim == 128) return by_rg<kFP8, 128>(rg, a, s, ev, per_cu);
-    if (kv_dtype == kFP8 && dim == 64) return by_rg<kFP8, 64>(rg, a, s, ev, per_cu);
+hipError_t dispatch_m(int kv_dtype, int dim, const GqaArgs* a, hipStream_t s, const KernelEvents& ev, int* per_cu) {
+    if (kv_dtype == kBF16 && dim == 128) return launch_m<kBF16, 128>(a, s, ev, per_cu);
+    if (kv_dtype == kBF16 && dim == 64) return launch_m<kBF16, 64>(a, s, ev, per_cu);
+    if (kv_dtype == kFP8 && dim == 128) return launch_m<kFP8, 128>(a, s, ev, per_cu);
+    if (kv_dtype == kFP8 && dim == 64) return launch_m<kFP8, 64>(a, s, ev, per_cu);
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_gqa_mfma(int kv_dtype, int head_dim, const GqaArgs& a, hipStream_t s, const KernelEvents& ev) {
-    return dispatch_m(kv_dtype, head_dim, a.group_log2, &a, s, ev, nullptr);
+    return dispatch_m(kv_dtype, head_dim, &a, s, ev, nullptr);
 }
 
-int gqa_mfma_workers_per_cu(int kv_dtype, int head_dim, int group_log2) {
+int gqa_mfma_workers_per_cu(int kv_dtype, int head_dim) {
     int per_cu = 0;
-    if (dispatch_m(kv_dtype, head_dim, group_log2, nullptr, nullptr, KernelEvents{}, &per_cu) != hipSuccess) return 0;
+    if (dispatch_m(kv_dtype, head_dim, nullptr, nullptr, KernelEvents{}, &per_cu) != hipSuccess) return 0;
     return per_cu;
 }
 

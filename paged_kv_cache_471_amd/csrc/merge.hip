@@ -36,7 +36,7 @@ constexpr float kFloor = -3.0e38f;
 // as the general path below.
 template <int NC>
 __device__ __forceinline__ void fold_columns(const MergeArgs& a, int t, int b, int j, int h0, int n, int gf,
-                                             int64_t start, int64_t W, int A, int heads, int gmask, int d4_log2) {
+                                             int64_t start, int64_t W, int A, int heads, int d4_log2) {
     const int D = a.dim;
     const int G = a.group;
     int hh[NC], ccol[NC];
@@ -47,8 +47,8 @@ __device__ __forceinline__ void fold_columns(const MergeArgs& a, int t, int b, i
         hh[u] = c >> d4_log2;
         ccol[u] = c - (hh[u] << d4_log2);
         const int slot_h = h0 + hh[u];
-        orow[u] = (static_cast<int64_t>(b) * a.rows + (slot_h >> a.group_log2)) * heads + (j << a.group_log2) +
-                  (slot_h & gmask);
+        const int r = slot_h / a.heads_per_unit;
+        orow[u] = (static_cast<int64_t>(b) * a.rows + r) * heads + j * a.heads_per_unit + (slot_h - r * a.heads_per_unit);
     }
     float m[NC], z[NC];
     float4 acc[NC];
@@ -83,7 +83,7 @@ __device__ __forceinline__ void fold_columns(const MergeArgs& a, int t, int b, i
     }
 #pragma unroll
     for (int u = 0; u < NC; ++u) {
-        if (((h0 + hh[u]) >> a.group_log2) >= a.rows) continue;
+        if ((h0 + hh[u]) / a.heads_per_unit >= a.rows) continue;
         const float inv = z[u] > 0.0f ? 1.0f / z[u] : 0.0f;
         if (a.out_is_bf16) {
             const uint32_t lo = f32_to_bf16_bits(acc[u].x * inv) | (static_cast<uint32_t>(f32_to_bf16_bits(acc[u].y * inv)) << 16);
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     const int blk = blockIdx.x / a.col_chunks;
     const int s = blk / per_stream;
     const int h0 = (blk % per_stream) * nh;
-    if ((h0 >> a.group_log2) >= a.rows) return;          // members that only pad the group
+    if (h0 / a.heads_per_unit >= a.rows) return;         // members that only pad the group
     const int b = s / a.units;
     const int j = s % a.units;
     // independent loads first: length, stream record, plan summary
@@ -132,15 +132,14 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     const int cols = C4 < kThreads ? C4 : kThreads;       // columns handled at once
     const int PL = kThreads / cols;                       // piece lanes per column
     const int q = t / cols;
-    const int heads = a.units << a.group_log2;            // query heads per row
-    const int gmask = (1 << a.group_log2) - 1;
+    const int heads = a.units * a.heads_per_unit;        // query heads per row
     const int d4_log2 = __builtin_ctz(static_cast<unsigned>(D)) - 2;   // D is a power of two
     if (C4 == 4 * kThreads && a.col_chunks == 1) {
-        fold_columns<4>(a, t, b, j, h0, n, gf, start, W, A, heads, gmask, d4_log2);
+        fold_columns<4>(a, t, b, j, h0, n, gf, start, W, A, heads, d4_log2);
         return;
     }
     if (C4 == 2 * kThreads && a.col_chunks == 1) {
-        fold_columns<2>(a, t, b, j, h0, n, gf, start, W, A, heads, gmask, d4_log2);
+        fold_columns<2>(a, t, b, j, h0, n, gf, start, W, A, heads, d4_log2);
         return;
     }
     for (int c0 = 0; c0 < C4; c0 += cols) {
@@ -148,8 +147,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
         const int h = c >> d4_log2;
         const int cc = c - (h << d4_log2);                // float4 column within the head
         const int slot_h = h0 + h;                        // (row, head) slot of the stream
-        const int r = slot_h >> a.group_log2;
-        const int64_t out_row = (static_cast<int64_t>(b) * a.rows + r) * heads + (j << a.group_log2) + (slot_h & gmask);
+        const int r = slot_h / a.heads_per_unit;
+        const int64_t out_row =
+            (static_cast<int64_t>(b) * a.rows + r) * heads + j * a.heads_per_unit + (slot_h - r * a.heads_per_unit);
         float m = -__builtin_inff(), z = 0.0f;
         float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll 8

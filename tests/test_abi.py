@@ -58,6 +58,7 @@ FAKE = 0x10000   # never dereferenced: every case below fails validation first
     (dict(q_dtype=1, kv_dtype=2), -1),                # fp8 without scales
     (dict(num_q_heads=64, num_kv_heads=2), -4),       # group 32 not offered
     (dict(num_q_heads=32, num_kv_heads=2), -4),       # group 16 with fp32 queries: no kernel
+    (dict(num_q_heads=6, num_kv_heads=2), -4),        # group 3 with fp32 queries: no kernel
     (dict(batch=-1), -2),
     (dict(num_pages=0), -2),
     (dict(batch=100000), -4),

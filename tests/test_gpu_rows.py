@@ -75,6 +75,33 @@ def test_rows_parity(q_dtype, kv_dtype, D, shape):
     _run_case(q_dtype, kv_dtype, D, Hq, Hkv, n, LENS, seed=Hq + 3 * Hkv + n + D)
 
 
+# groups that are not a power of two (bf16 queries, the matrix-core kernel):
+# (Hq, Hkv, rows), members = rows * Hq / Hkv padded to a power of two
+ODD_GROUPS = [
+    (28, 4, 1),    # g 7 (a 28/4 head shape), 7 members padded to 8
+    (40, 8, 1),    # g 5
+    (12, 2, 1),    # g 6
+    (24, 2, 1),    # g 12, padded to 16
+    (3, 1, 1),     # g 3, one KV head
+    (28, 4, 2),    # g 7, 14 members (MTP depth 1)
+    (15, 5, 3),    # g 3, 9 members padded to 16
+    (10, 2, 3),    # g 5, 15 members
+]
+
+
+@pytest.mark.parametrize("kv_dtype", [BF16, FP8])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("shape", ODD_GROUPS)
+def test_groups_not_a_power_of_two(kv_dtype, D, shape):
+    Hq, Hkv, n = shape
+    _run_case(BF16, kv_dtype, D, Hq, Hkv, n, LENS, seed=5 * Hq + Hkv + 7 * n + D)
+
+
+@pytest.mark.parametrize("workers", [1, 5, 333])
+def test_group_of_seven_under_forced_splits(workers):
+    _run_case(BF16, BF16, 128, 28, 4, 2, LENS, workers=workers, seed=70 + workers)
+
+
 @pytest.mark.parametrize("workers", [1, 3, 64, 2000])
 @pytest.mark.parametrize("shape", [(8, 2, 2), (4, 4, 8), (16, 8, 3), (8, 2, 4)])
 def test_rows_parity_under_forced_splits(workers, shape):

@@ -68,11 +68,11 @@ GQA_DTYPES = [(F32, F32), (BF16, BF16), (BF16, FP8)]
 
 def _gqa_shape(rng, q_dtype):
     """(Hq, Hkv, D, rows) with a kernel: (row, head) members per KV head at most
-    8 for fp32 queries and 16 for bf16 ones."""
+    8 for fp32 queries and 16 for bf16 ones; bf16 groups of any size."""
     limit = 8 if q_dtype == F32 else 16
     while True:
         Hkv = int(rng.choice([1, 2, 4, 8]))
-        g = int(rng.choice([1, 2, 4, 8, 16]))
+        g = int(rng.choice([1, 2, 4, 8, 16] if q_dtype == F32 else [1, 2, 3, 4, 5, 6, 7, 8, 12, 16]))
         n = int(rng.integers(1, 5))
         members = 1
         while members < n * g:
