@@ -231,13 +231,18 @@ def fp8_v_tile_index(page_size: int, head_dim: int) -> np.ndarray:
 
 
 def fp8_v_to_storage(v: np.ndarray) -> np.ndarray:
-    """Logical fp8 V codes [..][P][D] -> the tiled storage of the same shape."""
+    """Logical fp8 V codes [..][P][D] -> the tiled storage of the same shape.
+    The byte formula of fp8_v_tile_index is an axis permutation: with
+    t = 16 a + 4 b + c and d = DL e + 4 f + g, storage is ordered
+    [a][f][b][e][g][c], so one transpose lays it out."""
     P, D = v.shape[-2:]
-    idx = fp8_v_tile_index(P, D).reshape(-1)
-    flat = v.reshape(v.shape[:-2] + (P * D,))
-    out = np.empty_like(flat)
-    out[..., idx] = flat
-    return out.reshape(v.shape)
+    fp8_v_tile_index(P, D)                                   # validates the shape
+    DL = D // 16
+    lead = v.shape[:-2]
+    x = v.reshape(lead + (P // 16, 4, 4, 16, DL // 4, 4))   # a, b, c, e, f, g
+    n = len(lead)
+    x = x.transpose(tuple(range(n)) + (n, n + 4, n + 1, n + 3, n + 5, n + 2))
+    return np.ascontiguousarray(x).reshape(v.shape)
 
 
 def fp8_v_from_storage(v: np.ndarray) -> np.ndarray:
