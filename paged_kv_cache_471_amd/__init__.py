@@ -113,9 +113,15 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> Optional[int]:
+def _stream(stream, device_index: int = -1) -> Optional[int]:
+    """The HIP stream handle to launch on: the given stream (a torch stream or
+    a raw handle), else torch's current stream on device `device_index` (the
+    current device when negative), read as a raw handle without building a
+    Stream object."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        if device_index < 0:
+            device_index = torch.cuda.current_device()
+        return torch._C._cuda_getCurrentRawStream(device_index)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
@@ -153,63 +159,76 @@ def _want(cond: bool, msg: str):
 
 def _check_index_args(B: int, page_table: torch.Tensor, seq_lens: torch.Tensor, what: str = "seq_lens"):
     """page_table int32 [B][max_pages] and seq_lens (or positions) int32 [B]."""
-    _want(page_table.dtype == torch.int32 and page_table.dim() == 2 and page_table.shape[0] == B,
-          f"page_table must be int32 [{B}][max_pages], got {page_table.dtype} {tuple(page_table.shape)}")
-    _want(page_table.shape[1] >= 1, "page_table needs at least one column")
-    _want(seq_lens.dtype == torch.int32 and tuple(seq_lens.shape) == (B,),
-          f"{what} must be int32 [{B}], got {seq_lens.dtype} {tuple(seq_lens.shape)}")
+    pts = page_table.shape
+    if not (page_table.dtype == torch.int32 and len(pts) == 2 and pts[0] == B):
+        raise ValueError(f"page_table must be int32 [{B}][max_pages], got {page_table.dtype} {tuple(pts)}")
+    if pts[1] < 1:
+        raise ValueError("page_table needs at least one column")
+    if not (seq_lens.dtype == torch.int32 and seq_lens.shape == (B,)):
+        raise ValueError(f"{what} must be int32 [{B}], got {seq_lens.dtype} {tuple(seq_lens.shape)}")
 
 
 def _check_out_lse(out: Optional[torch.Tensor], lse: Optional[torch.Tensor], out_shape, out_dtype, lse_shape):
-    if out is not None:
-        _want(out.dtype == out_dtype and tuple(out.shape) == tuple(out_shape),
-              f"out must be {out_dtype} {tuple(out_shape)}, got {out.dtype} {tuple(out.shape)}")
-    if lse is not None:
-        _want(lse.dtype == torch.float32 and tuple(lse.shape) == tuple(lse_shape),
-              f"lse must be float32 {tuple(lse_shape)}, got {lse.dtype} {tuple(lse.shape)}")
+    if out is not None and not (out.dtype == out_dtype and out.shape == out_shape):
+        raise ValueError(f"out must be {out_dtype} {tuple(out_shape)}, got {out.dtype} {tuple(out.shape)}")
+    if lse is not None and not (lse.dtype == torch.float32 and lse.shape == lse_shape):
+        raise ValueError(f"lse must be float32 {tuple(lse_shape)}, got {lse.dtype} {tuple(lse.shape)}")
 
 
 def _check_paged_args(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
                       out: Optional[torch.Tensor], lse: Optional[torch.Tensor], k_scale, v_scale):
     """Shapes and dtypes of a GQA call, q [B][Hq][D] or [B][n][Hq][D]; raises
     ValueError before any pointer reaches the library (which sees only
-    pointers and the descriptor)."""
-    _want(q.dim() in (3, 4), f"q must be [B][Hq][D] or [B][rows][Hq][D], got {tuple(q.shape)}")
-    _want(q.dtype in (torch.float32, torch.bfloat16), f"q must be float32 or bfloat16, got {q.dtype}")
-    B, Hq, D = q.shape[0], q.shape[-2], q.shape[-1]
-    _want(kv_pages.dim() == 5 and kv_pages.shape[1] == 2 and kv_pages.shape[4] == D,
-          f"kv_pages must be [num_pages][2][Hkv][P][{D}], got {tuple(kv_pages.shape)}")
-    Hkv = kv_pages.shape[2]
-    _want(Hkv >= 1 and Hq % Hkv == 0, f"{Hq} query heads are not a multiple of {Hkv} KV heads")
-    fp8 = kv_pages.dtype in _FP8
-    if q.dtype == torch.float32:
-        _want(kv_pages.dtype == torch.float32, f"float32 q needs a float32 cache, got {kv_pages.dtype}")
-    else:
-        _want(kv_pages.dtype == torch.bfloat16 or fp8,
-              f"bfloat16 q needs a bfloat16 or fp8-e4m3 cache, got {kv_pages.dtype}")
+    pointers and the descriptor).  Messages are formatted only on failure."""
+    qs = q.shape
+    if len(qs) not in (3, 4):
+        raise ValueError(f"q must be [B][Hq][D] or [B][rows][Hq][D], got {tuple(qs)}")
+    qd = q.dtype
+    if qd is not torch.float32 and qd is not torch.bfloat16:
+        raise ValueError(f"q must be float32 or bfloat16, got {qd}")
+    B, Hq, D = qs[0], qs[-2], qs[-1]
+    ks = kv_pages.shape
+    if not (len(ks) == 5 and ks[1] == 2 and ks[4] == D):
+        raise ValueError(f"kv_pages must be [num_pages][2][Hkv][P][{D}], got {tuple(ks)}")
+    Hkv = ks[2]
+    if not (Hkv >= 1 and Hq % Hkv == 0):
+        raise ValueError(f"{Hq} query heads are not a multiple of {Hkv} KV heads")
+    kd = kv_pages.dtype
+    fp8 = kd in _FP8
+    if qd is torch.float32:
+        if kd is not torch.float32:
+            raise ValueError(f"float32 q needs a float32 cache, got {kd}")
+    elif not (kd is torch.bfloat16 or fp8):
+        raise ValueError(f"bfloat16 q needs a bfloat16 or fp8-e4m3 cache, got {kd}")
     if fp8:
         for name, sc in (("k_scale", k_scale), ("v_scale", v_scale)):
-            _want(sc is not None and sc.dtype == torch.float32 and tuple(sc.shape) == (Hkv,),
-                  f"an fp8 cache needs {name} float32 [{Hkv}], got "
-                  f"{None if sc is None else (sc.dtype, tuple(sc.shape))}")
-    else:
-        _want(k_scale is None and v_scale is None, "k_scale / v_scale apply to fp8 caches only")
+            if not (sc is not None and sc.dtype == torch.float32 and sc.shape == (Hkv,)):
+                raise ValueError(f"an fp8 cache needs {name} float32 [{Hkv}], got "
+                                 f"{None if sc is None else (sc.dtype, tuple(sc.shape))}")
+    elif k_scale is not None or v_scale is not None:
+        raise ValueError("k_scale / v_scale apply to fp8 caches only")
     _check_index_args(B, page_table, seq_lens)
-    _check_out_lse(out, lse, q.shape, q.dtype, q.shape[:-1])
+    _check_out_lse(out, lse, qs, qd, qs[:-1])
 
 
 def _check_mla_args(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
                     v_dim: int, out: Optional[torch.Tensor], lse: Optional[torch.Tensor]):
     """Shapes and dtypes of an MLA call, q [B][H][576] or [B][n][H][576]."""
-    _want(q.dim() in (3, 4), f"q must be [B][H][Dk] or [B][rows][H][Dk], got {tuple(q.shape)}")
-    _want(q.dtype == torch.bfloat16, f"MLA q must be bfloat16, got {q.dtype}")
-    Dk = q.shape[-1]
-    _want(kv_pages.dim() == 3 and kv_pages.dtype == torch.bfloat16,
-          f"MLA kv_pages must be bfloat16 [num_pages][P][{Dk}], got {kv_pages.dtype} {tuple(kv_pages.shape)}")
-    _want(kv_pages.shape[2] == Dk, f"the cache's latent width {kv_pages.shape[2]} differs from q's {Dk}")
-    _want(1 <= v_dim <= Dk, f"v_dim {v_dim} must lie in [1, {Dk}]")
-    _check_index_args(q.shape[0], page_table, seq_lens)
-    _check_out_lse(out, lse, tuple(q.shape[:-1]) + (v_dim,), torch.bfloat16, q.shape[:-1])
+    qs = q.shape
+    if len(qs) not in (3, 4):
+        raise ValueError(f"q must be [B][H][Dk] or [B][rows][H][Dk], got {tuple(qs)}")
+    if q.dtype is not torch.bfloat16:
+        raise ValueError(f"MLA q must be bfloat16, got {q.dtype}")
+    Dk = qs[-1]
+    ks = kv_pages.shape
+    if not (len(ks) == 3 and kv_pages.dtype is torch.bfloat16):
+        raise ValueError(f"MLA kv_pages must be bfloat16 [num_pages][P][{Dk}], got {kv_pages.dtype} {tuple(ks)}")
+    if ks[2] != Dk:
+        raise ValueError(f"the cache's latent width {ks[2]} differs from q's {Dk}")
+    if not (1 <= v_dim <= Dk):
+        raise ValueError(f"v_dim {v_dim} must lie in [1, {Dk}]")
+    _check_index_args(qs[0], page_table, seq_lens)
+    _check_out_lse(out, lse, qs[:-1] + (v_dim,), torch.bfloat16, qs[:-1])
 
 
 def paged_desc(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor, *, k_scale=None, v_scale=None,
@@ -231,7 +250,8 @@ def decode_attn_paged(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch
     float8_e4m3fn/uint8 with k_scale/v_scale [Hkv] fp32); page_table int32
     [B][max_pages]; seq_lens int32 [B].
     Returns (out [B][Hq][D] in q's dtype, lse [B][Hq] fp32 or None)."""
-    _want(q.dim() == 3, f"q must be [B][Hq][D], got {tuple(q.shape)}")
+    if q.dim() != 3:
+        raise ValueError(f"q must be [B][Hq][D], got {tuple(q.shape)}")
     _check_paged_args(q, kv_pages, page_table, seq_lens, out, lse, k_scale, v_scale)
     _need_cuda(q, kv_pages, page_table, seq_lens, k_scale, v_scale)
     if out is None:
@@ -241,7 +261,7 @@ def decode_attn_paged(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch
     _need_cuda(out, lse)
     d = paged_desc(q, kv_pages, page_table, k_scale=k_scale, v_scale=v_scale, workers=workers)
     st = _lib.decode_attn_paged(ctypes.byref(d), _ptr(q), _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens),
-                                float(scale), _ptr(out), _ptr(lse), _stream(stream))
+                                float(scale), _ptr(out), _ptr(lse), _stream(stream, q.get_device()))
     _check(st, "decode_attn_paged")
     return out, lse
 
@@ -267,7 +287,7 @@ def decode_attn_paged_rows(q: torch.Tensor, kv_pages: torch.Tensor, page_table: 
     _need_cuda(out, lse)
     d = paged_desc(q[:, 0], kv_pages, page_table, k_scale=k_scale, v_scale=v_scale, workers=workers)
     st = _lib.decode_attn_paged_rows(ctypes.byref(d), n, _ptr(q), _ptr(kv_pages), _ptr(page_table),
-                                     _ptr(seq_lens), float(scale), _ptr(out), _ptr(lse), _stream(stream))
+                                     _ptr(seq_lens), float(scale), _ptr(out), _ptr(lse), _stream(stream, q.get_device()))
     _check(st, "decode_attn_paged_rows")
     return out, lse
 
@@ -278,7 +298,8 @@ def decode_attn_mla(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.T
                     want_lse: bool = True, stream=None):
     """Absorbed MLA decode.  q bf16 [B][H][576]; kv_pages bf16 [num_pages][P][576].
     Returns (out bf16 [B][H][v_dim], lse fp32 [B][H] or None)."""
-    _want(q.dim() == 3, f"q must be [B][H][Dk], got {tuple(q.shape)}")
+    if q.dim() != 3:
+        raise ValueError(f"q must be [B][H][Dk], got {tuple(q.shape)}")
     _check_mla_args(q, kv_pages, page_table, seq_lens, v_dim, out, lse)
     _need_cuda(q, kv_pages, page_table, seq_lens)
     B, H, Dk = q.shape
@@ -290,7 +311,7 @@ def decode_attn_mla(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.T
     num_pages, P, Dk2 = kv_pages.shape
     d = MLADesc(B, H, Dk, v_dim, P, num_pages, page_table.shape[1], workers)
     st = _lib.decode_attn_mla(ctypes.byref(d), _ptr(q), _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens),
-                              float(scale), _ptr(out), _ptr(lse), _stream(stream))
+                              float(scale), _ptr(out), _ptr(lse), _stream(stream, q.get_device()))
     _check(st, "decode_attn_mla")
     return out, lse
 
@@ -315,7 +336,7 @@ def decode_attn_mla_rows(q: torch.Tensor, kv_pages: torch.Tensor, page_table: to
     num_pages, P, Dk2 = kv_pages.shape
     d = MLADesc(B, H, Dk, v_dim, P, num_pages, page_table.shape[1], workers)
     st = _lib.decode_attn_mla_rows(ctypes.byref(d), n, _ptr(q), _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens),
-                                   float(scale), _ptr(out), _ptr(lse), _stream(stream))
+                                   float(scale), _ptr(out), _ptr(lse), _stream(stream, q.get_device()))
     _check(st, "decode_attn_mla_rows")
     return out, lse
 
@@ -331,7 +352,7 @@ def decode_attn_plan(seq_lens: torch.Tensor, page_size: int, units: int, workers
     active, cuts, cursors = z(1), z(workers + 1), z(workers + 1, 4)
     fw, count = z(B * units), z(B * units)
     st = _lib.decode_attn_plan(B, _ptr(seq_lens), page_size, units, workers, _ptr(active), _ptr(cuts),
-                               _ptr(cursors), _ptr(fw), _ptr(count), _stream(stream))
+                               _ptr(cursors), _ptr(fw), _ptr(count), _stream(stream, seq_lens.get_device()))
     _check(st, "decode_attn_plan")
     return dict(active=active, cuts=cuts, cursors=cursors, first_worker=fw, piece_count=count)
 
@@ -353,7 +374,7 @@ def paged_kv_gather(kv_pages: torch.Tensor, page_table: torch.Tensor, seq_lens: 
         dense = torch.zeros((B, maxp * P, 2, Hkv, D), dtype=kv_pages.dtype, device=kv_pages.device)
         d = PagedDesc(B, Hkv, Hkv, D, P, num_pages, maxp, DA_F32, dtype_tag(kv_pages), 0, None, None)
     st = _lib.paged_kv_gather(ctypes.byref(d), 1 if mla else 0, _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens),
-                              _ptr(dense), _stream(stream))
+                              _ptr(dense), _stream(stream, kv_pages.get_device()))
     _check(st, "paged_kv_gather")
     return dense
 
@@ -384,7 +405,7 @@ def decode_kv_append(k_new: torch.Tensor, v_new: torch.Tensor, kv_pages: torch.T
     d = PagedDesc(B, Hkv, Hkv, D, P, num_pages, page_table.shape[1], dtype_tag(k_new), dtype_tag(kv_pages), 0,
                   _ptr(k_scale), _ptr(v_scale))
     st = _lib.decode_kv_append(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(kv_pages), _ptr(page_table),
-                               _ptr(positions), _stream(stream))
+                               _ptr(positions), _stream(stream, kv_pages.get_device()))
     _check(st, "decode_kv_append")
     return kv_pages
 
@@ -404,7 +425,7 @@ def decode_kv_append_mla(latent_new: torch.Tensor, kv_pages: torch.Tensor, page_
     _need_cuda(latent_new, kv_pages, page_table, positions)
     d = MLADesc(B, 128, Dk, 512, P, num_pages, page_table.shape[1], 0)
     st = _lib.decode_kv_append_mla(ctypes.byref(d), _ptr(latent_new), _ptr(kv_pages), _ptr(page_table),
-                                   _ptr(positions), _stream(stream))
+                                   _ptr(positions), _stream(stream, kv_pages.get_device()))
     _check(st, "decode_kv_append_mla")
     return kv_pages
 
@@ -454,7 +475,7 @@ def decode_attn_paged_ws(q: torch.Tensor, kv_pages: torch.Tensor, page_table: to
     nbytes = workspace.numel() * workspace.element_size()
     st = _lib.decode_attn_paged_ws(ctypes.byref(d), q4.shape[1], _ptr(q), _ptr(kv_pages), _ptr(page_table),
                                    _ptr(seq_lens), float(scale), _ptr(out), _ptr(lse), _ptr(workspace), nbytes,
-                                   _stream(stream))
+                                   _stream(stream, q.get_device()))
     _check(st, "decode_attn_paged_ws")
     return out, lse
 
@@ -477,7 +498,7 @@ def decode_attn_paged_noalloc(q: torch.Tensor, kv_pages: torch.Tensor, page_tabl
     q4 = _rows_view(q)
     d = paged_desc(q4[:, 0], kv_pages, page_table, k_scale=k_scale, v_scale=v_scale, workers=workers)
     st = _lib.decode_attn_paged_noalloc(ctypes.byref(d), q4.shape[1], _ptr(q), _ptr(kv_pages), _ptr(page_table),
-                                        _ptr(seq_lens), float(scale), _ptr(out), _ptr(lse), _stream(stream))
+                                        _ptr(seq_lens), float(scale), _ptr(out), _ptr(lse), _stream(stream, q.get_device()))
     _check(st, "decode_attn_paged_noalloc")
     return out, lse
 
@@ -497,7 +518,7 @@ def decode_attn_mla_ws(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torc
     d = MLADesc(B, H, Dk, v_dim, P, num_pages, page_table.shape[1], workers)
     nbytes = workspace.numel() * workspace.element_size()
     st = _lib.decode_attn_mla_ws(ctypes.byref(d), n, _ptr(q), _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens),
-                                 float(scale), _ptr(out), _ptr(lse), _ptr(workspace), nbytes, _stream(stream))
+                                 float(scale), _ptr(out), _ptr(lse), _ptr(workspace), nbytes, _stream(stream, q.get_device()))
     _check(st, "decode_attn_mla_ws")
     return out, lse
 
@@ -509,9 +530,9 @@ def validate_inputs(desc, page_table: torch.Tensor, seq_lens: torch.Tensor, stre
     _need_cuda(page_table, seq_lens)
     if isinstance(desc, MLADesc):
         return _lib.decode_attn_validate_inputs(None, ctypes.byref(desc), _ptr(page_table), _ptr(seq_lens),
-                                                _stream(stream))
+                                                _stream(stream, page_table.get_device()))
     return _lib.decode_attn_validate_inputs(ctypes.byref(desc), None, _ptr(page_table), _ptr(seq_lens),
-                                            _stream(stream))
+                                            _stream(stream, page_table.get_device()))
 
 
 def timer_begin(max_launches: int):

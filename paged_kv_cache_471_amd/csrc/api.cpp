@@ -212,6 +212,8 @@ void timer_release() {
 
 struct DeviceInfo {
     int num_cus = 0;
+    // workers per CU of each kernel variant (occupancy queries), by variant key
+    std::map<uint32_t, int> per_cu;
 };
 std::mutex g_dev_mutex;
 std::map<int, DeviceInfo> g_dev;
@@ -227,6 +229,35 @@ int device_cus(int* cus) {
         if (e != hipSuccess) return hip_fail(e);
     }
     *cus = d.num_cus;
+    return DA_OK;
+}
+
+// Compute units of the current device and the workers per CU of the variant
+// named by `key`, which `query` reports (0 = no such variant).  Both are
+// fixed for a device and a build, so each is asked once per process and
+// device; a failed query (0) is not kept.
+template <typename Query>
+int device_workers(uint32_t key, Query query, int* cus, int* per_cu) {
+    int st = device_cus(cus);
+    if (st != DA_OK) return st;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    {
+        std::lock_guard<std::mutex> lock(g_dev_mutex);
+        auto& m = g_dev[dev].per_cu;
+        auto it = m.find(key);
+        if (it != m.end()) {
+            *per_cu = it->second;
+            return DA_OK;
+        }
+    }
+    const int v = query();
+    if (v > 0) {
+        std::lock_guard<std::mutex> lock(g_dev_mutex);
+        g_dev[dev].per_cu[key] = v;
+    }
+    *per_cu = v;
     return DA_OK;
 }
 
@@ -308,12 +339,20 @@ int resolve_gqa_workers(const da_paged_desc* d, int members, bool mfma, int* G) 
         *G = d->workers;
         return DA_OK;
     }
-    int cus = 0;
-    int st = device_cus(&cus);
-    if (st != DA_OK) return st;
     const int group_log2 = __builtin_ctz(static_cast<unsigned>(d->num_q_heads / d->num_kv_heads));
-    const int per_cu = mfma ? da::gqa_mfma_workers_per_cu(d->kv_dtype, d->head_dim)
-                            : da::gqa_workers_per_cu(d->q_dtype, d->kv_dtype, d->head_dim, members, group_log2);
+    // variant key: kernel family, dtypes, head dim, members, group
+    const uint32_t key = (mfma ? 1u : 0u) | (static_cast<uint32_t>(d->q_dtype) << 1) |
+                         (static_cast<uint32_t>(d->kv_dtype) << 4) | (static_cast<uint32_t>(d->head_dim) << 7) |
+                         (static_cast<uint32_t>(members) << 16) | (static_cast<uint32_t>(group_log2) << 24);
+    int cus = 0, per_cu = 0;
+    int st = device_workers(
+        key,
+        [&] {
+            return mfma ? da::gqa_mfma_workers_per_cu(d->kv_dtype, d->head_dim)
+                        : da::gqa_workers_per_cu(d->q_dtype, d->kv_dtype, d->head_dim, members, group_log2);
+        },
+        &cus, &per_cu);
+    if (st != DA_OK) return st;
     if (per_cu <= 0) return DA_ERR_UNSUPPORTED;
     int g = cus * per_cu;
     if (g > da::kMaxWorkers) g = da::kMaxWorkers;
@@ -341,11 +380,14 @@ int resolve_mla_workers(const da_mla_desc* d, int* G) {
         *G = d->workers;
         return DA_OK;
     }
-    int cus = 0;
-    int st = device_cus(&cus);
+    const bool wave = d->num_heads == da::kMlaWaveHeads;
+    // variant keys above every GQA key (bit 31): the two MLA kernels
+    const uint32_t key = (1u << 31) | (wave ? 1u : 0u);
+    int cus = 0, per_cu = 0;
+    int st = device_workers(
+        key, [&] { return wave ? da::mla_wave_blocks_per_cu() : da::mla_blocks_per_cu(); }, &cus, &per_cu);
     if (st != DA_OK) return st;
-    int g = d->num_heads == da::kMlaWaveHeads ? cus * da::mla_wave_blocks_per_cu()
-                                              : cus * da::mla_blocks_per_cu() / da::mla_blocks_per_worker(d->num_heads);
+    int g = wave ? cus * per_cu : cus * per_cu / da::mla_blocks_per_worker(d->num_heads);
     if (g <= 0) return DA_ERR_UNSUPPORTED;
     if (g > da::kMlaMaxWorkers) g = da::kMlaMaxWorkers;
     *G = g;
