@@ -113,15 +113,21 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+# torch's current stream as a raw handle, without building a Stream object
+# (about 0.1 us against 2.7 us per call); absent from some torch builds
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream, device_index: int = -1) -> Optional[int]:
     """The HIP stream handle to launch on: the given stream (a torch stream or
     a raw handle), else torch's current stream on device `device_index` (the
-    current device when negative), read as a raw handle without building a
-    Stream object."""
+    current device when negative)."""
     if stream is None:
         if device_index < 0:
             device_index = torch.cuda.current_device()
-        return torch._C._cuda_getCurrentRawStream(device_index)
+        if _RAW_STREAM is not None:
+            return _RAW_STREAM(device_index)
+        return torch.cuda.current_stream(device_index).cuda_stream
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
