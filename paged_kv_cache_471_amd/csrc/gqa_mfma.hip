@@ -17,26 +17,23 @@
 //  * The result leaves lane (R, C) with tokens 4R..4R+3 of member C: the
 //    online softmax of a member runs over the four lanes of its column (two
 //    row swaps), in fp32.
-//  * Values (bf16 and fp32 caches): O[16 members][D] += P[16 members][16
-//    tokens] . V[16 tokens][D] with v_mfma_f32_16x16x4_f32: fp32 weights and
-//    fp32 values, in four steps of four tokens.  Step i takes token 4R + i
-//    from lane row R, so each lane's own weights are its A operand and V
-//    loaded as tokens 4R + i, dims [C D/16, (C+1) D/16) is the B operand, with
-//    no data movement.
-//  * Values (fp8 cache): O^T[D][16 members] += V^T[D][16 tokens] . P^T[16
-//    tokens][16 members] with v_mfma_f32_16x16x16_bf16, D / 16 dim blocks.
-//    Each fp32 weight is split into two bf16 terms, hi = bf16(p) and lo =
-//    bf16(p - hi), so hi + lo equals p to within 2^-17 relative; both terms
-//    meet the same values (fp8 codes convert to bf16 exactly) in two
+//  * Values: O^T[D][16 members] += V^T[D][16 tokens] . P^T[16 tokens][16
+//    members] with v_mfma_f32_16x16x16_bf16, D / 16 dim blocks.  Each fp32
+//    weight is split into two bf16 terms, hi = bf16(p) and lo = bf16(p - hi),
+//    so hi + lo equals p to within 2^-17 relative; both terms meet the same
+//    values (bf16 as stored; fp8 codes convert to bf16 exactly) in two
 //    products, exact in fp32 and accumulated in fp32.  The B operand of lane
 //    (R, C) is tokens 4R..4R+3 of member C: exactly the weights that lane
 //    holds after the softmax.  The A operand of dim block b is, for those four
-//    tokens, the code of dim C D/16 + b; the cache keeps fp8 V blocks in
-//    16-token tiles (fp8_v_byte in da_common.h) so that word b of the lane's
-//    16-byte pieces is exactly those four codes.  Row C of block b is thus
-//    dim C D/16 + b, and lane (R, C) ends holding member C's dims
-//    [4R D/16, 4R D/16 + 4 D/16): 16 dim blocks of 32-cycle fp32 steps per
-//    page become D/16 pairs of 8-cycle bf16 steps.
+//    tokens, the value of dim C D/16 + b.  bf16: the lane loads tokens 4R + i
+//    (i < 4), dims [C D/16, (C+1) D/16) as whole-row pieces, so block b takes
+//    one 16-bit half of word b / 2 of each of its four token rows (two
+//    register-local packs).  fp8: the cache keeps V blocks in 16-token tiles
+//    (fp8_v_byte in da_common.h) so that word b of the lane's 16-byte pieces
+//    is exactly those four codes.  Row C of block b is thus dim C D/16 + b,
+//    and lane (R, C) ends holding member C's dims [4R D/16, 4R D/16 + 4 D/16):
+//    per page, D/16 pairs of 8-cycle bf16 steps (an fp32 product on
+//    v_mfma_f32_16x16x4_f32 would take D/16 x 4 steps of 32 cycles).
 //  * Members are the q_rows x (q_heads / kv_heads) (row, head) pairs of a KV
 //    head, up to 16; unused member columns carry zero queries and are never
 //    written.  Row r of a request sees positions up to len - q_rows + r.
@@ -74,9 +71,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ floatx4_t mfma_s(bf16x8_t a, bf16x8_t b, floatx4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ floatx4_t mfma_v(float a, float b, floatx4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 typedef short short4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ floatx4_t mfma_v16(short4_t a, short4_t b, floatx4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -113,8 +107,9 @@ struct MCfg {
     static constexpr int KW = D * EB / 64 * 4;        // K words per lane: 4 lanes share a token row
     static constexpr int DL = D / 16;                 // value dims per lane
     static constexpr int VW = DL * EB / 4;            // V words per lane per token
-    // page buffers: two pages in flight, one for bf16 at head_dim 128, so that
-    // two waves fit on a SIMD (256 registers each, accumulators included)
+    // page buffers (NB - 1 pages in flight while one is computed): bf16 at
+    // head dim 128 keeps one in flight (two measured equal or slower on the
+    // llama8b batch, at 198 against 166 vector registers)
     static constexpr int NB = (EB == 2 && D == 128) ? 2 : 3;
 };
 
@@ -181,8 +176,8 @@ __device__ __forceinline__ int k_dim(int s, int R) {
 // stream busy, and a third only adds pieces to the merge (long-context
 // workload 96.0-96.8 against 102.7-103.2 us per step; every fp8 shape
 // measured was equal or faster).  bf16 keeps the compiler's own allocation
-// (about 200 registers plus 32 accumulation registers, two waves per SIMD); a
-// tighter bound that allows three made it 4-5 % slower.
+// (166 vector and 32 accumulation registers at head dim 128, two waves per
+// SIMD); a tighter bound that allows three made it 4-5 % slower.
 template <int KV>
 struct MOcc {
     static constexpr int blocks_per_cu = KV == kFP8 ? 3 : 1;
@@ -304,7 +299,7 @@ __global__ __launch_bounds__(kGqaBlock, MOcc<KV>::blocks_per_cu) void gqa_mfma_k
     };
 
     float m_run, l_run;                           // member Cc, replicated over the column
-    floatx4_t acc[DL];                            // O[member 4R + x][dim Cc DL + t] in acc[t][x]
+    floatx4_t acc[DL];                            // O[member Cc][dim 4R DL + DL x + t] in acc[t][x]
     auto reset = [&]() {
         m_run = kMaxInit;
         l_run = 0.0f;
@@ -370,63 +365,49 @@ __global__ __launch_bounds__(kGqaBlock, MOcc<KV>::blocks_per_cu) void gqa_mfma_k
         l_run = __builtin_fmaf(l_run, alpha, psum);
         m_run = mn;
         if (__ballot(alpha != 1.0f) != 0ull) {
+            // accumulator columns are members: this lane's own factor
+#pragma unroll
+            for (int t = 0; t < DL; ++t)
+#pragma unroll
+                for (int x = 0; x < 4; ++x) acc[t][x] *= alpha;
+        }
+        // ---- values: weights as bf16 hi + lo, the B operand (tokens 4R..4R+3 of member Cc)
+        const uint32_t h01 = bf16x2_rne(p[0], p[1]);
+        const uint32_t h23 = bf16x2_rne(p[2], p[3]);
+        const uint32_t l01 = bf16x2_rne(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
+        const uint32_t l23 = bf16x2_rne(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
+        const short4_t bh = as_short4(h01, h23);
+        const short4_t bl = as_short4(l01, l23);
+        auto block = [&](auto KB) {
+            constexpr int db = decltype(KB)::value;
+            short4_t av;                                             // dim Cc DL + db, tokens 4R..4R+3
             if constexpr (KV == kFP8) {
-                // accumulator columns are members: this lane's own factor
-#pragma unroll
-                for (int t = 0; t < DL; ++t)
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) acc[t][x] *= alpha;
+                const uint32_t codes = buf.v[db / VW].w[db % VW];
+                av = as_short4(fp8x2_to_bf16x2<false>(codes), fp8x2_to_bf16x2<true>(codes));
             } else {
-                // accumulator rows are members 4R + x: their factors sit in columns 4R + x
-                float al[4];
-#pragma unroll
-                for (int x = 0; x < 4; ++x) al[x] = __shfl(alpha, 4 * R + x, 64);
-#pragma unroll
-                for (int t = 0; t < DL; ++t)
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) acc[t][x] *= al[x];
+                // word db / 2 of token 4R + i holds dims Cc DL + 2 (db / 2) + {0, 1} in its
+                // low and high halves: gather this dim's half of the four tokens
+                constexpr int w = db / 2;
+                if constexpr ((db & 1) == 0)
+                    av = as_short4((buf.v[0].w[w] & 0xffffu) | (buf.v[1].w[w] << 16),
+                                   (buf.v[2].w[w] & 0xffffu) | (buf.v[3].w[w] << 16));
+                else
+                    av = as_short4((buf.v[0].w[w] >> 16) | (buf.v[1].w[w] & 0xffff0000u),
+                                   (buf.v[2].w[w] >> 16) | (buf.v[3].w[w] & 0xffff0000u));
             }
-        }
-        if constexpr (KV == kFP8) {
-            // ---- values: weights as bf16 hi + lo, the B operand (tokens 4R..4R+3 of member Cc)
-            const uint32_t h01 = bf16x2_rne(p[0], p[1]);
-            const uint32_t h23 = bf16x2_rne(p[2], p[3]);
-            const uint32_t l01 = bf16x2_rne(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
-            const uint32_t l23 = bf16x2_rne(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
-            const short4_t bh = as_short4(h01, h23);
-            const short4_t bl = as_short4(l01, l23);
-            auto block = [&](auto KB) {
-                constexpr int db = decltype(KB)::value;
-                const uint32_t codes = buf.v[db / VW].w[db % VW];    // dim Cc DL + db, tokens 4R..4R+3
-                const short4_t av = as_short4(fp8x2_to_bf16x2<false>(codes), fp8x2_to_bf16x2<true>(codes));
-                acc[db] = mfma_v16(av, bh, acc[db]);
-                acc[db] = mfma_v16(av, bl, acc[db]);
-            };
-            static_for<DL>(block);
-        } else {
-            // ---- values: step i, token 4R + i
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float vf[DL];
-#pragma unroll
-                for (int w = 0; w < VW; ++w) {
-                    vf[2 * w] = bf16_lo(buf.v[i].w[w]);
-                    vf[2 * w + 1] = bf16_hi(buf.v[i].w[w]);
-                }
-#pragma unroll
-                for (int t = 0; t < DL; ++t) acc[t] = mfma_v(p[i], vf[t], acc[t]);
-            }
-        }
+            acc[db] = mfma_v16(av, bh, acc[db]);
+            acc[db] = mfma_v16(av, bl, acc[db]);
+        };
+        static_for<DL>(block);
     };
 
-    // write the piece: member 4R + x, dims [Cc DL, Cc DL + DL); with an fp8
-    // cache member Cc, dims [4R DL, 4R DL + 4 DL) (dim 4R DL + DL x + t in acc[t][x])
+    // write the piece: member Cc, dims [4R DL, 4R DL + 4 DL) (dim 4R DL + DL x + t in acc[t][x])
     auto finalize = [&](bool whole, int slot) {
         const bool seen = l_run > 0.0f;
         const float inv_col = seen ? vsc / l_run : 0.0f;
         const float lse2 = seen ? m_run + __builtin_log2f(l_run) : -__builtin_inff();
-        if constexpr (KV == kFP8) {
-            if (mlive) {
+        if (mlive) {
+            {
                 const int d0 = 4 * R * DL;
                 if (whole) {
                     const int64_t row = (static_cast<int64_t>(cc.b) * NR + mrow) * Hq + cc.j * gs + mhead;
@@ -449,29 +430,6 @@ __global__ __launch_bounds__(kGqaBlock, MOcc<KV>::blocks_per_cu) void gqa_mfma_k
                             acc[(4 * e + 2) % DL][(4 * e + 2) / DL] * inv_col,
                             acc[(4 * e + 3) % DL][(4 * e + 3) / DL] * inv_col};
                 }
-            }
-        }
-#pragma unroll
-        for (int x = 0; x < (KV == kFP8 ? 0 : 4); ++x) {
-            const int mem = 4 * R + x;
-            const float inv = __shfl(inv_col, mem, 64);
-            const int mem_row = mem / gs;
-            if (mem_row >= NR) continue;
-            if (whole) {
-                const int64_t row =
-                    (static_cast<int64_t>(cc.b) * NR + mem_row) * Hq + cc.j * gs + (mem - mem_row * gs);
-                uint16_t* dst = static_cast<uint16_t*>(a.out) + row * D + Cc * DL;
-                uint32_t packed[DL / 2];
-#pragma unroll
-                for (int t = 0; t < DL / 2; ++t)
-                    packed[t] = f32_to_bf16_bits(acc[2 * t][x] * inv) |
-                                (static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * t + 1][x] * inv)) << 16);
-#pragma unroll
-                for (int t = 0; t < DL / 2; ++t) reinterpret_cast<uint32_t*>(dst)[t] = packed[t];
-            } else {
-                float* dst = a.o_part + (static_cast<int64_t>(slot) * MT + mem) * D + Cc * DL;
-#pragma unroll
-                for (int t = 0; t < DL; ++t) dst[t] = acc[t][x] * inv;
             }
         }
         if (R == 0 && mlive) {
