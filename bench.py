@@ -93,7 +93,7 @@ def gqa_kernel_name(cfg, rows: int = 1) -> str:
     elif (cfg.q_heads // cfg.kv_heads) & (cfg.q_heads // cfg.kv_heads - 1):   # group not a power of two
         mfma = cfg.q_dtype == wl.BF16 and members <= 16
     else:
-        mfma = cfg.q_dtype == wl.BF16 and 4 <= members <= 16
+        mfma = cfg.q_dtype == wl.BF16 and 2 <= members <= 16
         if os.environ.get("DA_GQA_VECTOR") == "1" and members <= 8:
             mfma = False
     return "gqa_mfma_kernel" if mfma else "gqa_attn_kernel"

@@ -105,12 +105,12 @@ extern "C" {
  * {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)}.  For fp8, k_scale and v_scale are device fp32
  * [num_kv_heads]; a stored code x of KV head j means e4m3(x) * scale[j].
  *
- * Kernels: bf16 queries with 4 to 16 query heads (or, with several query
+ * Kernels: bf16 queries with 2 to 16 query heads (or, with several query
  * rows, row x head pairs) per KV head run on the matrix cores (scores and
- * values as MFMA products, softmax weights kept in fp32, split into two bf16
- * terms for the fp8 value product); fp8 caches run there for every group
- * size, and so do groups that are not a power of two; fp32 queries and
- * bf16 groups of 1 or 2 on the vector ALUs.  Both
+ * values as MFMA products, softmax weights computed in fp32 and split into
+ * two bf16 terms for the value product); fp8 caches run there for every
+ * group size, and so do groups that are not a power of two; fp32 queries
+ * and a single bf16 query head per KV head on the vector ALUs.  Both
  * give the same semantics and the same tolerances; kv_pages must be 16-byte
  * aligned on the matrix-core path.
  *

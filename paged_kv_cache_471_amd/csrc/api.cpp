@@ -294,12 +294,14 @@ int check_paged(const da_paged_desc* d) {
     return DA_OK;
 }
 
-// Groups of 4 to 16 (row, head) members with bf16 queries run on the
+// Groups of 2 to 16 (row, head) members with bf16 queries run on the
 // matrix-core kernel (gqa_mfma.hip): from 8 query heads per K/V page up the
-// vector kernel is bound by its ALUs, and at 4 the matrix-core kernel still
-// measured 1-3 % faster (less vector work beside the loads).  Smaller bf16
-// groups and fp32 queries run on the vector kernel (gqa.hip); fp8 caches run
-// on the matrix-core kernel for every group size.
+// vector kernel is bound by its ALUs, and at 4 and 2 the matrix-core kernel
+// measured 4 % faster (less vector work beside the loads; llama8b lengths,
+// 8 KV heads: 127.8 against 132.6 us at 4, 125.6 against 130.5 us at 2).  A
+// single member (one-row MHA) and fp32 queries run on the vector kernel
+// (gqa.hip), equal or 0.6 % faster there; fp8 caches run on the matrix-core
+// kernel for every group size.
 //
 // Profiling aid: DA_GQA_VECTOR=1 in the environment (read once per process)
 // sends every group the vector kernel can take (up to 8 members) to it, so
@@ -321,7 +323,7 @@ bool gqa_uses_mfma(const da_paged_desc* d, int q_rows) {
     const int group = d->num_q_heads / d->num_kv_heads;
     if ((group & (group - 1)) != 0) return d->q_dtype == DA_BF16 && want <= 16;
     if (want <= 8 && vector_forced()) return false;
-    return d->q_dtype == DA_BF16 && d->kv_dtype == DA_BF16 && want >= 4 && want <= 16;
+    return d->q_dtype == DA_BF16 && d->kv_dtype == DA_BF16 && want >= 2 && want <= 16;
 }
 
 // (row, head) members of one KV head's group in the GQA kernels: q_rows times
