@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import workloads as wl
-from helpers import gqa_to_dev, mla_to_dev, gqa_oracle, assert_close_gqa, out_to_f64, TOL_OUT, TOL_LSE
+from helpers import gqa_to_dev, mla_to_dev, gqa_oracle, assert_close_gqa, assert_out_close, out_to_f64, TOL_LSE
 
 pytestmark = pytest.mark.gpu
 
@@ -54,8 +54,7 @@ def test_mla_at_the_batch_limit():
     o = out_to_f64(out)
     l = lse.cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(o)), "non-finite output"
-    err = float(np.max(np.abs(o - ro)))
-    assert err <= TOL_OUT[wl.BF16], f"max |out - oracle| = {err:.3e}"
+    assert_out_close(o, ro, wl.BF16, True, f"batch {MAX_BATCH}")
     fin = np.isfinite(rl)
     assert np.array_equal(np.isfinite(l), fin) and np.all(l[~fin] == -np.inf), "empty requests: lse -inf"
     rel = np.abs(l[fin] - rl[fin]) / np.maximum(1.0, np.abs(rl[fin]))

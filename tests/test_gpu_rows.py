@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import workloads as wl
-from helpers import to_dev_storage, out_to_f64, TOL_OUT, TOL_LSE
+from helpers import to_dev_storage, out_to_f64, assert_out_close, TOL_LSE
 from oracle.formats import F32, BF16, FP8
 
 pytestmark = pytest.mark.gpu
@@ -42,8 +42,7 @@ def _run_case(q_dtype, kv_dtype, D, Hq, Hkv, n, lens, workers=0, seed=0, scale=N
     o = out_to_f64(out)
     l = lse.cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(o)), "non-finite output"
-    err = float(np.max(np.abs(o - ro)))
-    assert err <= TOL_OUT[kv_dtype], f"max |out - oracle| = {err:.3e}"
+    err = assert_out_close(o, ro, kv_dtype, q_dtype == BF16, "rows")
     fin = np.isfinite(rl)
     assert np.array_equal(np.isfinite(l), fin) and np.all(l[~fin] == -np.inf), "empty rows must give lse = -inf"
     rel = np.abs(l[fin] - rl[fin]) / np.maximum(1.0, np.abs(rl[fin]))
@@ -143,5 +142,5 @@ def test_mtp2_at_full_llama8b_size_whole():
     o = out_to_f64(out)
     l = lse.cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(l)), "non-finite output or lse"
-    assert np.max(np.abs(o - ro)) <= TOL_OUT[BF16]
+    assert_out_close(o, ro, BF16, True, "rows")
     assert np.max(np.abs(l - rl) / np.maximum(1.0, np.abs(rl))) <= TOL_LSE[BF16]

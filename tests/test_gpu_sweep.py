@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import workloads as wl
-from helpers import to_dev_storage, out_to_f64, TOL_OUT, TOL_LSE
+from helpers import to_dev_storage, out_to_f64, assert_out_close, TOL_LSE
 from oracle.formats import F32, BF16, FP8
 
 pytestmark = pytest.mark.gpu
@@ -50,12 +50,11 @@ def _lengths(rng, B, page):
     return np.maximum(lens, 0)
 
 
-def _check(out, lse, ro, rl, kvd, label):
+def _check(out, lse, ro, rl, kvd, label, out_bf16=True):
     o = out_to_f64(out)
     l = lse.cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(o)), f"{label}: non-finite output"
-    err = float(np.max(np.abs(o - ro))) if o.size else 0.0
-    assert err <= TOL_OUT[kvd], f"{label}: max |out - oracle| = {err:.3e}"
+    assert_out_close(o, ro, kvd, out_bf16, label)
     fin = np.isfinite(rl)
     assert np.array_equal(np.isfinite(l), fin) and np.all(l[~fin] == -np.inf), f"{label}: empty rows"
     if fin.any():
@@ -81,7 +80,9 @@ def _gqa_shape(rng, q_dtype):
             return g * Hkv, Hkv, int(rng.choice([64, 128])), n
 
 
-@pytest.mark.parametrize("seed", range(24))
+# seed 1363: sharp scale, an output of magnitude 4.05 whose correctly rounded
+# bf16 value is 1.552e-2 from the exact one (the bound of helpers.out_bound)
+@pytest.mark.parametrize("seed", list(range(24)) + [1363])
 def test_gqa_random(seed):
     rng = np.random.default_rng(7100 + seed)
     q_dtype, kv_dtype = GQA_DTYPES[seed % 3]
@@ -105,7 +106,7 @@ def test_gqa_random(seed):
     out, lse = da.decode_attn_paged_rows(qd, kv, pt, sl, case.scale, k_scale=ks, v_scale=vs, workers=workers)
     torch.cuda.synchronize()
     label = f"seed {seed}: q{q_dtype}/kv{kv_dtype} {Hq}/{Hkv} D{D} P{P} rows {n} B{B} G={workers} sharp={sharp}"
-    _check(out, lse, ro, rl, kv_dtype, label)
+    _check(out, lse, ro, rl, kv_dtype, label, out_bf16=q_dtype == BF16)
     if n == 1:
         out1, lse1 = da.decode_attn_paged(qd[:, 0].contiguous(), kv, pt, sl, case.scale, k_scale=ks, v_scale=vs,
                                           workers=workers)

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads as wl
-from helpers import gqa_oracle, assert_close_gqa, TOL_OUT, TOL_LSE
+from helpers import gqa_oracle, assert_close_gqa, assert_out_close, TOL_LSE
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 EXE = os.path.join(HERE, "native", "decode_caller")
@@ -117,8 +117,7 @@ def test_native_mla_call(tmp_path, H):
     o = out.float().numpy().astype(np.float64)
     l = lse.numpy().astype(np.float64)
     assert np.all(np.isfinite(o)), "non-finite output"
-    err = float(np.max(np.abs(o - ro)))
-    assert err <= TOL_OUT[wl.BF16], f"max |out - oracle| = {err:.3e}"
+    assert_out_close(o, ro, wl.BF16, True, "native decode_attn_mla")
     fin = np.isfinite(rl)
     assert np.array_equal(np.isfinite(l), fin) and np.all(l[~fin] == -np.inf)
     rel = np.abs(l[fin] - rl[fin]) / np.maximum(1.0, np.abs(rl[fin]))
