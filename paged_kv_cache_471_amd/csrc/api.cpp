@@ -574,6 +574,11 @@ int mla_step(const da_mla_desc* dd, int q_rows, const void* q, const void* kv_pa
         ra.rows = q_rows;
         ra.page_size = d->page_size;
         ra.max_pages = d->max_pages_per_seq;
+        // the 128-head kernel takes the rows row-major: the workers that run
+        // a request's rows then sit G / q_rows apart, on the same XCD when
+        // that distance is a multiple of 8, and stream the same latent pages
+        // at about the same time (the second read meets the caches)
+        ra.row_major = wave ? 1 : 0;
         hipError_t e = da::launch_rows_expand(ra, s);
         if (e != hipSuccess) return hip_fail(e);
         seq_lens = ra.lens_out;
@@ -598,6 +603,8 @@ int mla_step(const da_mla_desc* dd, int q_rows, const void* q, const void* kv_pa
     ma.o_part = sb.o_part;
     ma.lse_part = sb.lse_part;
     ma.o_tmp = tmp;
+    ma.row_batch = dd->batch;
+    ma.rows = wave ? q_rows : 1;
     if (wave) {
         hipError_t e = da::launch_mla_wave(ma, s, next_kernel_events());
         if (e != hipSuccess) return hip_fail(e);

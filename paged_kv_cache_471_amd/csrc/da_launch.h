@@ -80,6 +80,11 @@ struct MlaArgs {
     // tiles, lse_part [batch + workers][128][2] (running max in log2, sum),
     // and o_tmp [workers][128][512] as scratch.
     float* o_tmp;
+    // Several query rows per request (128-head kernel): request e of the
+    // expanded batch is row e / row_batch of request e % row_batch, whose q,
+    // out and lse rows sit at (e % row_batch) * rows + e / row_batch; rows = 1
+    // means request e itself.
+    int row_batch, rows;
 };
 
 // Log-sum-exp merge of the partial slots of split streams.  One workgroup per

@@ -73,6 +73,12 @@ constexpr int kPD = 4;                       // score operand K-blocks in flight
 constexpr int kVD = 4;                       // value operand dim blocks in flight
 static_assert(kKB == 2 * kLoadsPerWave, "one chunk load every second K-block");
 
+// Row of q, out and lse that request b of the (possibly row-expanded) batch
+// reads and writes (MlaArgs::row_batch, rows).
+__device__ __forceinline__ int64_t io_row(const MlaArgs& a, int b) {
+    return a.rows > 1 ? static_cast<int64_t>(b % a.row_batch) * a.rows + b / a.row_batch : b;
+}
+
 struct __align__(16) WaveSmem {
     char ring[kSlots][kMlaSlotBytes];
 };
@@ -168,10 +174,10 @@ __global__ __launch_bounds__(kBlock, 1) void mla_wave_kernel(MlaArgs a) {
     const WaveShare sh = plan_share(a.seq_lens, a.batch, P, 1, a.workers, g);
     if (sh.has_empty && w == 0) {
         for_each_empty_request(a.seq_lens, a.batch, a.workers, g, [&](int b) {
-            uint16_t* o = static_cast<uint16_t*>(a.out) + static_cast<int64_t>(b) * H * kMlaV;
+            uint16_t* o = static_cast<uint16_t*>(a.out) + io_row(a, b) * H * kMlaV;
             for (int e = lane; e < H * kMlaV; e += 64) o[e] = 0;
             if (a.lse != nullptr)
-                for (int h = lane; h < H; h += 64) a.lse[static_cast<int64_t>(b) * H + h] = -__builtin_inff();
+                for (int h = lane; h < H; h += 64) a.lse[io_row(a, b) * H + h] = -__builtin_inff();
         });
     }
     const int A = sh.active;
@@ -230,7 +236,7 @@ __global__ __launch_bounds__(kBlock, 1) void mla_wave_kernel(MlaArgs a) {
         for (int hb = 0; hb < kNHB; ++hb) {
             const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(
                 static_cast<const uint16_t*>(a.q) +
-                (static_cast<int64_t>(b) * H + kHW * w + 16 * hb + (ln & 15)) * kMlaLatent + 8 * (ln >> 4));
+                (io_row(a, b) * H + kHW * w + 16 * hb + (ln & 15)) * kMlaLatent + 8 * (ln >> 4));
 #pragma unroll
             for (int kb = 0; kb < kKB; ++kb) qreg[hb][kb] = src[kb * 4];
         }
@@ -651,10 +657,10 @@ __global__ __launch_bounds__(kMergeThreads) void mla_wave_merge_kernel(MlaArgs a
     if (a.lse != nullptr && db0 == 0 && l16 == 0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            a.lse[static_cast<int64_t>(b) * H + 16 * hblk + 4 * q + r] = (M[r] + __builtin_log2f(Z[r])) * kLn2;
+            a.lse[io_row(a, b) * H + 16 * hblk + 4 * q + r] = (M[r] + __builtin_log2f(Z[r])) * kLn2;
     }
     __syncthreads();
-    uint4* out = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(b) * H + 16 * hblk) * kMlaV);
+    uint4* out = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + (io_row(a, b) * H + 16 * hblk) * kMlaV);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int idx = t + kMergeThreads * u;            // 16 rows x 64 pieces of 8 values

@@ -18,9 +18,9 @@ namespace {
 constexpr int kRowsBlock = 128;
 
 __global__ __launch_bounds__(kRowsBlock) void rows_expand_kernel(RowsArgs a) {
-    const int r = blockIdx.x;                   // expanded request b * rows + i
-    const int b = r / a.rows;
-    const int i = r - b * a.rows;
+    const int r = blockIdx.x;                   // expanded request (see RowsArgs::row_major)
+    const int b = a.row_major ? r % a.batch : r / a.rows;
+    const int i = a.row_major ? r / a.batch : r - b * a.rows;
     const int L = a.seq_lens[b];
     const int len = max(0, L - a.rows + 1 + i);
     if (threadIdx.x == 0) a.lens_out[r] = len;
