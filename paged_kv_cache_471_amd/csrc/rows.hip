@@ -7,8 +7,12 @@
 // positions up to its own, so each row is a decode query over a history cut
 // at its own length.  This kernel writes, for each row, that length and a copy
 // of the request's page-table entries the row reads; the MLA attention and
-// merge kernels then run unchanged over batch * rows requests, whose queries
-// and outputs [batch][rows][heads][...] already sit in that order.
+// merge kernels then run over batch * rows requests.  In the request-major
+// order (b * rows + i) the queries and outputs [batch][rows][heads][...]
+// already sit in that order; in the row-major order (i * batch + b, taken by
+// the 128-head kernel) that kernel maps each request to its q / out row, and
+// the workers that hold one request's rows end up G / rows apart in the
+// plan, where they stream the same latent pages at about the same time.
 #include "da_common.h"
 #include "da_rows.h"
 
