@@ -85,18 +85,17 @@ def counters_from_profiles(path, sources):
 
 
 def gqa_kernel_name(cfg, rows: int = 1) -> str:
-    """The GQA attention kernel the library runs for this head shape."""
+    """The GQA attention kernel the library runs for this head shape (the
+    library's own host query, so that this never drifts from its dispatch)."""
     import workloads as wl
-    members = rows * cfg.q_heads // cfg.kv_heads
-    if cfg.kv_dtype == wl.FP8:          # fp8 V tiles are read by the matrix-core kernel only
-        mfma = cfg.q_dtype == wl.BF16 and members <= 16
-    elif (cfg.q_heads // cfg.kv_heads) & (cfg.q_heads // cfg.kv_heads - 1):   # group not a power of two
-        mfma = cfg.q_dtype == wl.BF16 and members <= 16
-    else:
-        mfma = cfg.q_dtype == wl.BF16 and 2 <= members <= 16
-        if os.environ.get("DA_GQA_VECTOR") == "1" and members <= 8:
-            mfma = False
-    return "gqa_mfma_kernel" if mfma else "gqa_attn_kernel"
+    import paged_kv_cache_471_amd as da
+    fp8 = cfg.kv_dtype == wl.FP8
+    d = da.PagedDesc(max(1, cfg.batch), cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.page_size, 1, 1,
+                     cfg.q_dtype, cfg.kv_dtype, 0, 16 if fp8 else None, 16 if fp8 else None)
+    name = da.kernel_name(d, rows)
+    if name is None:
+        raise ValueError(f"the library refuses this shape: {cfg}, {rows} rows")
+    return name
 
 
 def headline_kernel(cfg, rows: int, default_shape: bool):

@@ -373,6 +373,17 @@ int decode_attn_paged_noalloc(const da_paged_desc* desc, int32_t q_rows, const v
 int decode_attn_validate_inputs(const da_paged_desc* gqa_or_null, const da_mla_desc* mla_or_null,
                                 const int32_t* page_table, const int32_t* seq_lens, void* stream);
 
+/*
+ * decode_attn_kernel_name - the attention kernel a call with this descriptor
+ * and q_rows query rows runs ("gqa_mfma_kernel", "gqa_attn_kernel",
+ * "mla_wave_kernel" or "mla_attn_kernel"), as the same host checks and
+ * choice decide it; NULL when the call would be refused.  Exactly one of
+ * gqa / mla is non-NULL.  Host only: no device call, no allocation; the
+ * string is static.
+ */
+const char* decode_attn_kernel_name(const da_paged_desc* gqa_or_null, const da_mla_desc* mla_or_null,
+                                    int32_t q_rows);
+
 /* default number of workers for each path on the current device (host query). */
 int decode_attn_default_workers(const da_paged_desc* gqa_or_null, const da_mla_desc* mla_or_null,
                                 int32_t* workers);

@@ -27,7 +27,7 @@ EXPORTS = ("decode_attn_paged", "decode_attn_paged_rows", "decode_attn_mla", "de
            "decode_attn_default_workers", "decode_attn_status_str", "decode_attn_last_hip_error",
            "decode_attn_timer_begin", "decode_attn_timer_end",
            "decode_attn_workspace_size", "decode_attn_paged_ws", "decode_attn_mla_ws", "decode_attn_validate_inputs",
-           "decode_attn_paged_noalloc")
+           "decode_attn_paged_noalloc", "decode_attn_kernel_name")
 
 
 class PagedDesc(ctypes.Structure):
@@ -97,6 +97,8 @@ def _load():
     lib.decode_attn_paged_noalloc.restype = ctypes.c_int
     lib.decode_attn_validate_inputs.argtypes = [ctypes.POINTER(PagedDesc), ctypes.POINTER(MLADesc), vp, vp, vp]
     lib.decode_attn_validate_inputs.restype = ctypes.c_int
+    lib.decode_attn_kernel_name.argtypes = [ctypes.POINTER(PagedDesc), ctypes.POINTER(MLADesc), i32]
+    lib.decode_attn_kernel_name.restype = ctypes.c_char_p
     return lib
 
 
@@ -448,6 +450,17 @@ def default_workers(q: torch.Tensor = None, kv_pages: torch.Tensor = None, page_
     return int(out.value)
 
 
+def kernel_name(desc, q_rows: int = 1) -> Optional[str]:
+    """The attention kernel a call with this descriptor (PagedDesc or MLADesc)
+    and q_rows query rows runs, or None when the call would be refused (host
+    query)."""
+    if isinstance(desc, MLADesc):
+        r = _lib.decode_attn_kernel_name(None, ctypes.byref(desc), int(q_rows))
+    else:
+        r = _lib.decode_attn_kernel_name(ctypes.byref(desc), None, int(q_rows))
+    return None if r is None else r.decode()
+
+
 def _rows_view(q: torch.Tensor) -> torch.Tensor:
     """[B][Hq][D] -> [B][1][Hq][D]; [B][n][Hq][D] as is."""
     return q.unsqueeze(1) if q.dim() == 3 else q
@@ -558,4 +571,4 @@ __all__ = ["timer_begin", "timer_end", "decode_attn_paged", "decode_attn_paged_r
            "decode_attn_mla_rows", "decode_attn_plan", "paged_kv_gather", "default_workers",
            "PagedDesc", "MLADesc", "DecodeAttnError", "LIB_PATH", "EXPORTS", "lib", "decode_kv_append", "decode_kv_append_mla",
            "workspace_size", "decode_attn_paged_ws", "decode_attn_mla_ws", "validate_inputs",
-           "decode_attn_paged_noalloc", "NOALLOC_SCRATCH_BYTES"]
+           "decode_attn_paged_noalloc", "NOALLOC_SCRATCH_BYTES", "kernel_name"]

@@ -878,6 +878,17 @@ int paged_kv_gather(const da_paged_desc* d, int32_t mla, const void* kv_pages, c
     return DA_OK;
 }
 
+const char* decode_attn_kernel_name(const da_paged_desc* gqa, const da_mla_desc* mla, int32_t q_rows) {
+    if ((gqa == nullptr) == (mla == nullptr) || q_rows < 1 || q_rows > 16) return nullptr;
+    if (gqa != nullptr) {
+        // the same checks and choice as gqa_step
+        if (check_paged(gqa) != DA_OK || gqa_members(gqa, q_rows) == 0) return nullptr;
+        return gqa_uses_mfma(gqa, q_rows) ? "gqa_mfma_kernel" : "gqa_attn_kernel";
+    }
+    if (check_mla(mla) != DA_OK) return nullptr;
+    return mla->num_heads == da::kMlaWaveHeads ? "mla_wave_kernel" : "mla_attn_kernel";
+}
+
 int decode_attn_default_workers(const da_paged_desc* gqa, const da_mla_desc* mla, int32_t* workers) {
     if (workers == nullptr || (gqa == nullptr) == (mla == nullptr)) return DA_ERR_NULL;
     int G = 0;

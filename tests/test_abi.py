@@ -367,3 +367,37 @@ def test_binding_refuses_bad_append_arguments(lib):
         lib.decode_kv_append_mla(lat.float(), torch.zeros(6, 64, 576, dtype=torch.bfloat16), pt, pos)
     with pytest.raises(ValueError):
         lib.decode_kv_append_mla(lat, torch.zeros(6, 64, 576, dtype=torch.bfloat16), pt[:2], pos)
+
+
+@pytest.mark.parametrize("kw,rows,name", [
+    (dict(q_dtype=1, kv_dtype=1, num_q_heads=8, num_kv_heads=8), 1, "gqa_attn_kernel"),    # one head per KV head
+    (dict(q_dtype=1, kv_dtype=1, num_q_heads=16, num_kv_heads=8), 1, "gqa_mfma_kernel"),   # groups of two up
+    (dict(q_dtype=1, kv_dtype=1, num_q_heads=32, num_kv_heads=8), 1, "gqa_mfma_kernel"),
+    (dict(q_dtype=1, kv_dtype=1, num_q_heads=8, num_kv_heads=8), 2, "gqa_mfma_kernel"),    # 2 (row, head) pairs
+    (dict(q_dtype=1, kv_dtype=1, num_q_heads=24, num_kv_heads=8), 1, "gqa_mfma_kernel"),   # group of 3
+    (dict(q_dtype=1, kv_dtype=1, num_q_heads=128, num_kv_heads=8), 1, "gqa_mfma_kernel"),  # 16
+    (dict(q_dtype=1, kv_dtype=1, num_q_heads=128, num_kv_heads=8), 2, None),               # 32 pairs
+    (dict(q_dtype=1, kv_dtype=1, num_q_heads=256, num_kv_heads=8), 1, None),               # group of 32
+    (dict(q_dtype=0, kv_dtype=0, num_q_heads=32, num_kv_heads=8), 1, "gqa_attn_kernel"),   # fp32 queries
+    (dict(q_dtype=0, kv_dtype=0, num_q_heads=128, num_kv_heads=8), 1, None),               # fp32, 16 members
+    (dict(q_dtype=0, kv_dtype=0, num_q_heads=24, num_kv_heads=8), 1, None),                # fp32, group of 3
+    (dict(q_dtype=1, kv_dtype=2, num_q_heads=8, num_kv_heads=8, k_scale=FAKE, v_scale=FAKE), 1, "gqa_mfma_kernel"),
+    (dict(q_dtype=1, kv_dtype=2, num_q_heads=8, num_kv_heads=8), 1, None),                 # fp8 without scales
+    (dict(q_dtype=1, kv_dtype=1, num_q_heads=32, num_kv_heads=8), 0, None),
+    (dict(q_dtype=1, kv_dtype=1, num_q_heads=32, num_kv_heads=8), 17, None),
+])
+def test_kernel_name_follows_the_dispatch(lib, kw, rows, name):
+    """The host query names the kernel the call runs (or None when the call
+    is refused), with the same checks and choice."""
+    assert lib.kernel_name(_desc(lib, **kw), rows) == name
+
+
+def test_kernel_name_mla_and_argument_errors(lib):
+    assert lib.kernel_name(_mla_desc(lib), 1) == "mla_wave_kernel"
+    assert lib.kernel_name(_mla_desc(lib), 2) == "mla_wave_kernel"
+    assert lib.kernel_name(_mla_desc(lib, num_heads=16), 1) == "mla_attn_kernel"
+    assert lib.kernel_name(_mla_desc(lib, num_heads=48), 1) is None
+    L = lib.lib()
+    assert L.decode_attn_kernel_name(None, None, 1) is None
+    d, m = _desc(lib), _mla_desc(lib)
+    assert L.decode_attn_kernel_name(ctypes.byref(d), ctypes.byref(m), 1) is None
