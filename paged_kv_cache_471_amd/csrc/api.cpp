@@ -511,9 +511,12 @@ int gqa_step(const da_paged_desc* d, int q_rows, const void* q, const void* kv_p
     // workgroup per head, so that their pieces spread over more lanes, and
     // streams of more than 16 pieces (few long requests) also by column
     // chunks, down to 4 float4 columns per workgroup, so that each of a
-    // workgroup's threads folds about four pieces.
+    // workgroup's threads folds about four pieces.  Full 16-member groups
+    // split in up to 16 pieces merge two heads per workgroup (llama8b lengths
+    // at 128/8 heads: 142.0 against 145.5 us per step with one head; at 4 and
+    // 8 members one head measured best).
     const int pieces = ga.workers / (streams > 0 ? streams : 1);
-    ma.heads_per_block = pieces <= 2 && members * d->head_dim <= 4 * 128 ? members : 1;
+    ma.heads_per_block = pieces <= 2 && members * d->head_dim <= 4 * 128 ? members : (members >= 16 && pieces <= 16 ? 2 : 1);
     ma.col_chunks = 1;
     if (ma.heads_per_block == 1 && pieces > 16) {
         const int c4 = d->head_dim / 4;
