@@ -68,6 +68,14 @@ def test_mla_rows_parity_under_forced_splits(workers):
     _run(128, 2, [1, 2, 64, 65, 129, 700], workers=workers, seed=7 + workers)
 
 
+@pytest.mark.parametrize("n,workers", [(4, 0), (5, 37), (16, 0), (16, 256)])
+def test_mla_rows_many_rows(n, workers):
+    """Up to the 16-row limit on the 128-head kernel, whose expanded batch is
+    row-major (request e is row e / B of request e mod B): every row must
+    land in its own [b][row] slot of q, out and lse."""
+    _run(128, n, [0, 1, 5, 17, 33, 64, 65, 200, 901], workers=workers, seed=40 + n + workers)
+
+
 def test_mla_single_row_equals_decode_attn_mla():
     cfg = wl.MLAConfig("m1", 71, 6, 128, 576, 512, 64, "uniform:1:900")
     case = wl.make_mla_case(cfg, poison=True)
