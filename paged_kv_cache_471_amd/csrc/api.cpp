@@ -889,6 +889,8 @@ const char* decode_attn_kernel_name(const da_paged_desc* gqa, const da_mla_desc*
         return gqa_uses_mfma(gqa, q_rows) ? "gqa_mfma_kernel" : "gqa_attn_kernel";
     }
     if (check_mla(mla) != DA_OK) return nullptr;
+    // the same limit as mla_step: rows run as batch * q_rows requests
+    if (static_cast<int64_t>(mla->batch) * q_rows > da::kMaxBatch) return nullptr;
     return mla->num_heads == da::kMlaWaveHeads ? "mla_wave_kernel" : "mla_attn_kernel";
 }
 

@@ -397,6 +397,8 @@ def test_kernel_name_mla_and_argument_errors(lib):
     assert lib.kernel_name(_mla_desc(lib), 2) == "mla_wave_kernel"
     assert lib.kernel_name(_mla_desc(lib, num_heads=16), 1) == "mla_attn_kernel"
     assert lib.kernel_name(_mla_desc(lib, num_heads=48), 1) is None
+    assert lib.kernel_name(_mla_desc(lib, batch=8192), 1) == "mla_wave_kernel"
+    assert lib.kernel_name(_mla_desc(lib, batch=8192), 2) is None      # 16384 expanded requests
     L = lib.lib()
     assert L.decode_attn_kernel_name(None, None, 1) is None
     d, m = _desc(lib), _mla_desc(lib)
