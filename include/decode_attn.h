@@ -99,9 +99,10 @@ extern "C" {
  *
  * Offered: head_dim in {64, 128}; page_size 16, 32, 64, 128 or 256 (the
  * kernels walk 16-token tiles of a page); num_q_heads / num_kv_heads from
- * 1 to 16, with at most 16 (row, head) pairs per KV head on the matrix cores
- * and 8 on the vector ALUs; group sizes that are not a power of two, and
- * groups of 16, need bf16 queries (matrix cores); (q_dtype, kv_dtype) in
+ * 1 to 16 (a kernel takes at most 16 (row, head) pairs per KV head on the
+ * matrix cores and 8 on the vector ALUs; more query rows than that run in
+ * row blocks, see decode_attn_paged_rows); group sizes that are not a power
+ * of two, and groups of 16, need bf16 queries (matrix cores); (q_dtype, kv_dtype) in
  * {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)}.  For fp8, k_scale and v_scale are device fp32
  * [num_kv_heads]; a stored code x of KV head j means e4m3(x) * scale[j].
  *
@@ -186,14 +187,18 @@ int decode_attn_paged(const da_paged_desc* desc, const void* q, const void* kv_p
  * t <= seq_lens[b] - q_rows + i (causal among the new rows, older history
  * whole).  A row that sees no position (seq_lens[b] < q_rows - i) gets
  * out = 0 and lse = -inf.
- *   q_rows      1 .. 16, with q_rows * (Hq / Hkv) <= 16 for bf16 queries
- *               (groups of 8 to 16 (row, head) pairs run on the matrix cores)
- *               and <= 8 for fp32; DA_ERR_UNSUPPORTED beyond.
+ *   q_rows      1 .. 16.  When q_rows * (Hq / Hkv) exceeds a kernel's tile
+ *               (16 pairs on the matrix cores, 8 on the vector ALUs), the
+ *               rows run in blocks of the largest divisor of q_rows that
+ *               fits, each block a request of its own over the same pages
+ *               (the pages are then read once per block, and batch *
+ *               blocks must stay within the batch limit; the workspace holds
+ *               the blocks' lengths and page tables).
  *   q           device, [B][q_rows][Hq][D] q_dtype.
  *   out         device, [B][q_rows][Hq][D] q_dtype (written).
  *   lse         device, fp32 [B][q_rows][Hq] (written), or NULL.
  * Other arguments, layouts and errors as decode_attn_paged; each K/V page is
- * read once for all rows.
+ * read once for all rows of a block.
  */
 int decode_attn_paged_rows(const da_paged_desc* desc, int32_t q_rows, const void* q, const void* kv_pages,
                            const int32_t* page_table, const int32_t* seq_lens, float scale,

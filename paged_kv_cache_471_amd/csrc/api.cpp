@@ -396,20 +396,55 @@ int resolve_mla_workers(const da_mla_desc* d, int* G) {
     return DA_OK;
 }
 
+// Query rows per attention call of a GQA step with q_rows rows: all of them
+// when their (row, head) pairs fit a kernel's member tile, else the largest
+// divisor of q_rows that does.  A step whose rows are split runs as
+// batch * (q_rows / block) requests of block rows each, request-major
+// (b * blocks + k holds rows [k block, (k + 1) block) of request b), so the
+// q, out and lse rows of the expanded requests are those of [batch][q_rows]
+// in place and the kernels need no mapping; each expanded request's history
+// is cut where its last row's view ends.  0 when no block fits.
+int gqa_row_block(const da_paged_desc* d, int q_rows) {
+    for (int r = q_rows; r >= 1; --r)
+        if (q_rows % r == 0 && gqa_members(d, r) != 0) return r;
+    return 0;
+}
+
+// The descriptor of the attention calls of a GQA step (batch expanded when
+// its rows run in blocks) and their rows per request; DA_OK or a status.
+int gqa_call_shape(const da_paged_desc* d, int q_rows, da_paged_desc* call, int* block) {
+    *block = gqa_row_block(d, q_rows);
+    if (*block == 0) return DA_ERR_UNSUPPORTED;
+    *call = *d;
+    if (*block < q_rows) {
+        const int64_t expanded = static_cast<int64_t>(d->batch) * (q_rows / *block);
+        if (expanded > da::kMaxBatch) return DA_ERR_UNSUPPORTED;
+        call->batch = static_cast<int32_t>(expanded);
+        const int64_t units_bound =
+            static_cast<int64_t>(call->num_kv_heads) * call->batch * call->max_pages_per_seq * (call->page_size / 16);
+        if (units_bound >= (int64_t(1) << 31)) return DA_ERR_UNSUPPORTED;
+    }
+    return DA_OK;
+}
+
 // Workspace bytes of one call: the same checks, worker count and layout as
 // gqa_step / mla_step, so that a buffer of this size is always enough.
 int gqa_workspace_bytes(const da_paged_desc* d, int q_rows, size_t* bytes) {
     int st = check_paged(d);
     if (st != DA_OK) return st;
     if (q_rows < 1 || q_rows > 16) return q_rows < 1 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
-    const int members = gqa_members(d, q_rows);
-    if (members == 0) return DA_ERR_UNSUPPORTED;
-    *bytes = 0;
-    if (d->batch == 0) return DA_OK;
-    int G = 0;
-    st = resolve_gqa_workers(d, members, gqa_uses_mfma(d, q_rows), &G);
+    da_paged_desc cd;
+    int block = 0;
+    st = gqa_call_shape(d, q_rows, &cd, &block);
     if (st != DA_OK) return st;
-    *bytes = split_layout(d->batch * d->num_kv_heads, G, members, d->head_dim, nullptr, nullptr, 0);
+    const int members = gqa_members(&cd, block);
+    *bytes = 0;
+    if (cd.batch == 0) return DA_OK;
+    int G = 0;
+    st = resolve_gqa_workers(&cd, members, gqa_uses_mfma(&cd, block), &G);
+    if (st != DA_OK) return st;
+    const size_t extra = block < q_rows ? static_cast<size_t>(cd.batch) * (1 + cd.max_pages_per_seq) : 0;
+    *bytes = split_layout(cd.batch * cd.num_kv_heads, G, members, cd.head_dim, nullptr, nullptr, extra);
     return DA_OK;
 }
 
@@ -435,14 +470,19 @@ int mla_workspace_bytes(const da_mla_desc* dd, int q_rows, size_t* bytes) {
     return DA_OK;
 }
 
-int gqa_step(const da_paged_desc* d, int q_rows, const void* q, const void* kv_pages, const int32_t* page_table,
-             const int32_t* seq_lens, float scale, void* out, float* lse, void* stream,
+int gqa_step(const da_paged_desc* dd, int rows_total, const void* q, const void* kv_pages,
+             const int32_t* page_table, const int32_t* seq_lens, float scale, void* out, float* lse, void* stream,
              const CallerWorkspace* cws = nullptr) {
-    int st = check_paged(d);
+    int st = check_paged(dd);
     if (st != DA_OK) return st;
-    if (q_rows < 1 || q_rows > 16) return q_rows < 1 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
+    if (rows_total < 1 || rows_total > 16) return rows_total < 1 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
+    da_paged_desc cd;
+    int q_rows = 0;                                   // rows per request of the attention call
+    st = gqa_call_shape(dd, rows_total, &cd, &q_rows);
+    if (st != DA_OK) return st;
+    const da_paged_desc* d = &cd;
+    const bool blocked = q_rows < rows_total;
     const int members = gqa_members(d, q_rows);
-    if (members == 0) return DA_ERR_UNSUPPORTED;
     const bool mfma = gqa_uses_mfma(d, q_rows);
     if (q == nullptr || kv_pages == nullptr || page_table == nullptr || seq_lens == nullptr || out == nullptr)
         return DA_ERR_NULL;
@@ -462,8 +502,26 @@ int gqa_step(const da_paged_desc* d, int q_rows, const void* q, const void* kv_p
     const int group_log2 = __builtin_ctz(static_cast<unsigned>(group));
     const int streams = d->batch * d->num_kv_heads;
     SplitBuffers sb;
-    st = get_split_buffers(s, streams, G, members, d->head_dim, &sb, 0, cws);
+    const size_t extra = blocked ? static_cast<size_t>(d->batch) * (1 + d->max_pages_per_seq) : 0;
+    st = get_split_buffers(s, streams, G, members, d->head_dim, &sb, extra, cws);
     if (st != DA_OK) return st;
+    if (blocked) {
+        da::RowsArgs ra{};
+        ra.seq_lens = seq_lens;
+        ra.page_table = page_table;
+        ra.lens_out = sb.extra;
+        ra.table_out = sb.extra + d->batch;
+        ra.batch = dd->batch;
+        ra.rows = rows_total;
+        ra.block = q_rows;
+        ra.page_size = d->page_size;
+        ra.max_pages = d->max_pages_per_seq;
+        ra.row_major = 0;
+        hipError_t e = da::launch_rows_expand(ra, s);
+        if (e != hipSuccess) return hip_fail(e);
+        seq_lens = ra.lens_out;
+        page_table = ra.table_out;
+    }
 
     da::GqaArgs ga{};
     ga.q = q;
@@ -575,6 +633,7 @@ int mla_step(const da_mla_desc* dd, int q_rows, const void* q, const void* kv_pa
         ra.table_out = sb.extra + d->batch;
         ra.batch = dd->batch;
         ra.rows = q_rows;
+        ra.block = 1;
         ra.page_size = d->page_size;
         ra.max_pages = d->max_pages_per_seq;
         // the 128-head kernel takes the rows row-major: the workers that run
@@ -885,8 +944,10 @@ const char* decode_attn_kernel_name(const da_paged_desc* gqa, const da_mla_desc*
     if ((gqa == nullptr) == (mla == nullptr) || q_rows < 1 || q_rows > 16) return nullptr;
     if (gqa != nullptr) {
         // the same checks and choice as gqa_step
-        if (check_paged(gqa) != DA_OK || gqa_members(gqa, q_rows) == 0) return nullptr;
-        return gqa_uses_mfma(gqa, q_rows) ? "gqa_mfma_kernel" : "gqa_attn_kernel";
+        da_paged_desc cd;
+        int block = 0;
+        if (check_paged(gqa) != DA_OK || gqa_call_shape(gqa, q_rows, &cd, &block) != DA_OK) return nullptr;
+        return gqa_uses_mfma(&cd, block) ? "gqa_mfma_kernel" : "gqa_attn_kernel";
     }
     if (check_mla(mla) != DA_OK) return nullptr;
     // the same limit as mla_step: rows run as batch * q_rows requests

@@ -14,6 +14,9 @@ struct RowsArgs {
     int32_t* lens_out;          // [batch * rows]
     int32_t* table_out;         // [batch * rows][max_pages]; entries past a row's pages untouched
     int batch, rows, page_size, max_pages;
+    // rows per expanded request: request (b, k) holds rows [k block,
+    // (k + 1) block) of request b; 1 = every row a request of its own
+    int block;
     // 0: expanded request b * rows + i is row i of request b; 1: it is
     // i * batch + b (row-major over the rows, so that the same row of every
     // request forms one contiguous half, third, ... of the expanded batch)

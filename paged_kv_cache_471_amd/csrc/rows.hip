@@ -23,10 +23,13 @@ constexpr int kRowsBlock = 128;
 
 __global__ __launch_bounds__(kRowsBlock) void rows_expand_kernel(RowsArgs a) {
     const int r = blockIdx.x;                   // expanded request (see RowsArgs::row_major)
-    const int b = a.row_major ? r % a.batch : r / a.rows;
-    const int i = a.row_major ? r / a.batch : r - b * a.rows;
+    const int nb = a.rows / a.block;            // expanded requests per request
+    const int b = a.row_major ? r % a.batch : r / nb;
+    const int k = a.row_major ? r / a.batch : r - b * nb;
     const int L = a.seq_lens[b];
-    const int len = max(0, L - a.rows + 1 + i);
+    // the block's last row, k block + block - 1, sees positions up to
+    // L - rows + k block + block - 1
+    const int len = max(0, L - a.rows + (k + 1) * a.block);
     if (threadIdx.x == 0) a.lens_out[r] = len;
     const int pages = (len + a.page_size - 1) / a.page_size;
     const int32_t* src = a.page_table + static_cast<int64_t>(b) * a.max_pages;
@@ -37,7 +40,8 @@ __global__ __launch_bounds__(kRowsBlock) void rows_expand_kernel(RowsArgs a) {
 }  // namespace
 
 hipError_t launch_rows_expand(const RowsArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(rows_expand_kernel, dim3(a.batch * a.rows), dim3(kRowsBlock), 0, s, a);
+    if (a.block < 1 || a.rows % a.block != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(rows_expand_kernel, dim3(a.batch * (a.rows / a.block)), dim3(kRowsBlock), 0, s, a);
     return hipGetLastError();
 }
 

@@ -160,9 +160,10 @@ def test_append_null_and_misaligned_rejected(lib):
 @pytest.mark.parametrize("kw,rows,status", [
     (dict(), 0, -2),                                   # no rows
     (dict(), -1, -2),
-    (dict(), 9, -4),                                   # more rows than any kernel group holds
-    (dict(num_q_heads=8, num_kv_heads=2), 3, -4),      # 3 rows x 4 heads > 8 members
-    (dict(num_q_heads=8, num_kv_heads=1), 2, -4),      # 2 rows x 8 heads
+    (dict(), 17, -4),                                  # more rows than a step takes
+    (dict(num_q_heads=16, num_kv_heads=1), 1, -4),     # fp32: 16 heads per KV head fit no kernel
+    (dict(batch=8192, q_dtype=1, kv_dtype=1, num_q_heads=32, num_kv_heads=2), 2, -4),   # 2 x 16 pairs: rows
+                                                       # run in blocks of one, 16384 requests
     (dict(head_dim=96), 2, -4),                        # descriptor checks still apply
 ])
 def test_rows_rejected_before_any_device_call(lib, kw, rows, status):
@@ -376,7 +377,8 @@ def test_binding_refuses_bad_append_arguments(lib):
     (dict(q_dtype=1, kv_dtype=1, num_q_heads=8, num_kv_heads=8), 2, "gqa_mfma_kernel"),    # 2 (row, head) pairs
     (dict(q_dtype=1, kv_dtype=1, num_q_heads=24, num_kv_heads=8), 1, "gqa_mfma_kernel"),   # group of 3
     (dict(q_dtype=1, kv_dtype=1, num_q_heads=128, num_kv_heads=8), 1, "gqa_mfma_kernel"),  # 16
-    (dict(q_dtype=1, kv_dtype=1, num_q_heads=128, num_kv_heads=8), 2, None),               # 32 pairs
+    (dict(q_dtype=1, kv_dtype=1, num_q_heads=128, num_kv_heads=8), 2, "gqa_mfma_kernel"),  # 32 pairs: row blocks
+    (dict(q_dtype=0, kv_dtype=0, num_q_heads=8, num_kv_heads=2), 4, "gqa_attn_kernel"),    # fp32: blocks of 2 rows
     (dict(q_dtype=1, kv_dtype=1, num_q_heads=256, num_kv_heads=8), 1, None),               # group of 32
     (dict(q_dtype=0, kv_dtype=0, num_q_heads=32, num_kv_heads=8), 1, "gqa_attn_kernel"),   # fp32 queries
     (dict(q_dtype=0, kv_dtype=0, num_q_heads=128, num_kv_heads=8), 1, None),               # fp32, 16 members

@@ -68,10 +68,31 @@ SHAPES = [  # (Hq, Hkv, rows): members = rows * Hq / Hkv, padded to a power of t
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("shape", SHAPES)
 def test_rows_parity(q_dtype, kv_dtype, D, shape):
+    # fp32 queries with more than 8 (row, head) pairs run in row blocks
     Hq, Hkv, n = shape
-    if q_dtype == F32 and n * Hq // Hkv > 8:
-        pytest.skip("fp32 queries: groups of up to 8 (row, head) pairs")
     _run_case(q_dtype, kv_dtype, D, Hq, Hkv, n, LENS, seed=Hq + 3 * Hkv + n + D)
+
+
+# more (row, head) pairs than a kernel tile holds (16 on the matrix cores, 8 on
+# the vector ALUs): the rows run in blocks, each block a request of its own
+# over the same pages with its history cut where its last row's view ends
+# (Hq, Hkv, rows, q dtype, kv dtype)
+BLOCKED = [
+    (32, 2, 2, BF16, BF16),    # g 16 x 2 rows: blocks of 1 row
+    (128, 8, 2, BF16, FP8),    # the 128/8 head shape with MTP depth 1, fp8 cache
+    (16, 2, 3, BF16, BF16),    # g 8 x 3 rows: blocks of 1 (2 does not divide 3)
+    (8, 2, 8, BF16, BF16),     # g 4 x 8 rows: blocks of 4
+    (12, 4, 6, BF16, BF16),    # g 3 x 6 rows: blocks of 3 (9 pairs)
+    (8, 2, 4, F32, F32),       # fp32, g 4 x 4 rows: blocks of 2
+    (8, 1, 16, F32, F32),      # fp32, g 8 x 16 rows: blocks of 1
+]
+
+
+@pytest.mark.parametrize("workers", [0, 7])
+@pytest.mark.parametrize("shape", BLOCKED)
+def test_rows_in_blocks(shape, workers):
+    Hq, Hkv, n, qd, kd = shape
+    _run_case(qd, kd, 128, Hq, Hkv, n, LENS, workers=workers, seed=11 * Hq + Hkv + 3 * n + workers)
 
 
 # groups that are not a power of two (bf16 queries, the matrix-core kernel):
