@@ -35,6 +35,7 @@ def _bits(t):
     (wl.BF16, wl.BF16, 32, 8, 128, 1),       # the llama-8B head shape (matrix-core kernel)
     (wl.BF16, wl.FP8, 16, 2, 128, 2),        # fp8 with two query rows
     (wl.F32, wl.F32, 8, 2, 64, 1),           # vector kernel
+    (wl.BF16, wl.BF16, 32, 2, 128, 2),       # 2 rows x 16 heads: rows in blocks (expanded in the scratch)
 ])
 def test_noalloc_matches_allocating_entry_point(qd, kd, Hq, Hkv, D, rows):
     cfg = wl.GQAConfig("noalloc", 21, 12, Hq, Hkv, D, 16, qd, kd, "lognormal:900:1.0:1:6000")
