@@ -6,11 +6,12 @@ memory fill.  The captured step is replayed several times, with eager calls
 on another stream and device-wide waits between the replays, and every
 replay must equal the eager result bitwise (the kernels are deterministic;
 the eager result is itself checked against the oracle elsewhere)."""
+import numpy as np
 import pytest
 import torch
 
 import workloads as wl
-from helpers import gqa_to_dev, mla_to_dev
+from helpers import gqa_to_dev, mla_to_dev, to_dev_storage
 
 pytestmark = pytest.mark.gpu
 
@@ -90,6 +91,58 @@ def test_mla_step_replays_from_a_graph():
 
     def eager_other():
         da.decode_attn_mla(*args, 512, other_out)
+        assert torch.equal(_bits(other_out), _bits(ref_out))
+
+    _check_replays(step, out, lse, ref_out, ref_lse, eager_other)
+
+
+# several query rows per request: the call adds a row-expansion kernel (and,
+# past a tile's worth of (row, head) pairs, runs the rows in blocks), all of
+# it launches into the captured stream
+@pytest.mark.parametrize("kd,Hq,Hkv,n", [(wl.BF16, 32, 8, 2), (wl.FP8, 32, 8, 2), (wl.BF16, 32, 2, 4)])
+def test_gqa_rows_step_replays_from_a_graph(kd, Hq, Hkv, n):
+    cfg = wl.GQAConfig("graph", 14, 24, Hq, Hkv, 128, 16, wl.BF16, kd, "lognormal:1500:0.9:1:9000")
+    case = wl.make_gqa_case(cfg, poison=True, seed=63)
+    t = gqa_to_dev(case)
+    rng = np.random.default_rng(64)
+    q = to_dev_storage(wl.to_bf16_bits(rng.standard_normal((24, n, Hq, 128)).astype(np.float32)), wl.BF16)
+    args = (q, t["kv"], t["page_table"], t["seq_lens"], case.scale)
+    kw = dict(k_scale=t["k_scale"], v_scale=t["v_scale"])
+    ref_out, ref_lse = da.decode_attn_paged_rows(*args, **kw)
+    torch.cuda.synchronize()
+    out = torch.empty_like(ref_out)
+    lse = torch.empty_like(ref_lse)
+    other_out = torch.empty_like(ref_out)
+
+    def step():
+        da.decode_attn_paged_rows(*args, out, lse, **kw)
+
+    def eager_other():
+        da.decode_attn_paged_rows(*args, other_out, **kw)
+        assert torch.equal(_bits(other_out), _bits(ref_out))
+
+    _check_replays(step, out, lse, ref_out, ref_lse, eager_other)
+
+
+@pytest.mark.parametrize("n", [2, 4])
+def test_mla_rows_step_replays_from_a_graph(n):
+    cfg = wl.MLAConfig("graph", 15, 16, 128, 576, 512, 64, "lognormal:2500:0.8:64:12000")
+    case = wl.make_mla_case(cfg, seed=65)
+    t = mla_to_dev(case)
+    rng = np.random.default_rng(66)
+    q = to_dev_storage(wl.to_bf16_bits(rng.standard_normal((16, n, 128, 576)).astype(np.float32)), wl.BF16)
+    args = (q, t["kv"], t["page_table"], t["seq_lens"], case.scale)
+    ref_out, ref_lse = da.decode_attn_mla_rows(*args)
+    torch.cuda.synchronize()
+    out = torch.empty_like(ref_out)
+    lse = torch.empty_like(ref_lse)
+    other_out = torch.empty_like(ref_out)
+
+    def step():
+        da.decode_attn_mla_rows(*args, 512, out, lse)
+
+    def eager_other():
+        da.decode_attn_mla_rows(*args, 512, other_out)
         assert torch.equal(_bits(other_out), _bits(ref_out))
 
     _check_replays(step, out, lse, ref_out, ref_lse, eager_other)
